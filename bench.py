@@ -1,0 +1,347 @@
+#!/usr/bin/env python3
+"""Benchmark of the mixed-precision tiled attention prefill hot path on one
+MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input
+already resident in HBM: per-block quantisation of Q and K, the packed
+precision mask, and the dual-path attention forward.  Default workload: the
+Qwen3-8B-shaped prefill (batch 2, 32 query / 8 KV heads, head dim 128, 16k
+tokens, causal, bf16) with 25% of the mask groups on the bf16 path and int8
+elsewhere.
+
+Prints ONE JSON line on stdout.  `value` is the step's algorithmic TFLOP/s
+(QK^T 2d flops per valid score element on its path, plus 2d for each
+adaptively recomputed element, plus P V 2d per valid element); `roofline`
+describes the attention kernel alone against the mix-weighted MFMA roofline
+T_roof = 2d N8 / P8 + 2d (N16 + Nflag) / P16 + 2d Nvalid / P16 with MI355X's
+published dense peaks P8 = 5.0e15 (int8 / fp8) and P16 = 2.5e15 (bf16 /
+fp16); `cpu_baseline` times the CPU oracle on a bounded sample of the same
+workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK8 = 5.0e15      # MI355X dense int8 / fp8 MFMA, ops/s
+PEAK16 = 2.5e15     # MI355X dense bf16 / fp16 MFMA, flop/s
+KERNEL_SOURCES = ["mixed_precision_tiled_amd/csrc/attn_kernel.h",
+                  "mixed_precision_tiled_amd/csrc/lamp_device.h",
+                  "mixed_precision_tiled_amd/csrc/attn_d64.hip",
+                  "mixed_precision_tiled_amd/csrc/attn_d128.hip",
+                  "mixed_precision_tiled_amd/csrc/attn_d256.hip"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# valid-element counts per path (roofline input), from the mask the GPU built
+# ---------------------------------------------------------------------------
+
+def tile_valid_counts(S_q, S_k, tile_m, tile_n, causal):
+    """[n_qt, n_kt] number of valid (query, key) pairs in each score tile."""
+    n_qt, n_kt = -(-S_q // tile_m), -(-S_k // tile_n)
+    r0 = np.arange(n_qt) * tile_m
+    r1 = np.minimum(S_q, r0 + tile_m)                 # rows [r0, r1)
+    c0 = np.arange(n_kt) * tile_n
+    c1 = np.minimum(S_k, c0 + tile_n)                 # cols [c0, c1)
+    if not causal:
+        return np.outer(r1 - r0, c1 - c0).astype(np.int64)
+    cnt = np.zeros((n_qt, n_kt), dtype=np.int64)
+    for a in range(n_qt):
+        rows = np.arange(r0[a], r1[a])
+        # valid keys per row within the tile: clip(row + 1, c0, c1) - c0
+        cnt[a] = (np.clip(rows[:, None] + 1, c0[None, :], c1[None, :]) - c0[None, :]).sum(0)
+    return cnt
+
+
+def route_counts(mask_words, S_q, S_k, tile_m, tile_n, tiles_per_bit, causal, flags=None):
+    """dict(n8, n16, nflag, nvalid) from packed mask words [B, Hq, n_qt, W]."""
+    mw = np.asarray(mask_words, dtype=np.uint64)
+    n_kt = -(-S_k // tile_n)
+    g = np.arange(n_kt) // tiles_per_bit
+    bits = ((mw[..., g // 64] >> (g % 64).astype(np.uint64)) & np.uint64(1)).astype(np.int64)
+    cnt = tile_valid_counts(S_q, S_k, tile_m, tile_n, causal)       # [n_qt, n_kt]
+    n8 = int((bits * cnt[None, None]).sum())
+    nvalid = int(cnt.sum()) * mw.shape[0] * mw.shape[1]
+    nflag = 0
+    if flags is not None:
+        # flags [B, Hq, n_sb, FW]: sub-block of 32 rows x key tile
+        fw = np.asarray(flags, dtype=np.uint64)
+        kt = np.arange(n_kt)
+        fb = ((fw[..., kt // 64] >> (kt % 64).astype(np.uint64)) & np.uint64(1)).astype(np.int64)
+        sub = tile_valid_counts(S_q, S_k, 32, tile_n, causal)         # [n_sb, n_kt]
+        nflag = int((fb * sub[None, None]).sum())
+    return dict(n8=n8, n16=nvalid - n8, nflag=nflag, nvalid=nvalid)
+
+
+def algorithmic_flops(c, D):
+    return 2.0 * D * (c["n8"] + c["n16"] + c["nflag"]) + 2.0 * D * c["nvalid"]
+
+
+def roofline_time(c, D):
+    return 2.0 * D * c["n8"] / PEAK8 + 2.0 * D * (c["n16"] + c["nflag"]) / PEAK16 + \
+        2.0 * D * c["nvalid"] / PEAK16
+
+
+# ---------------------------------------------------------------------------
+# traffic from the committed rocprofv3 counter summary of this kernel
+# ---------------------------------------------------------------------------
+
+def committed_traffic(workload):
+    path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", txt)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_sha or not m_b or m_sha.group(1) != kernel_source_hash():
+        return None
+    return float(m_b.group(1))
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline (bounded sample of the same workload)
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(cfg, q, k, v, budget_s=12.0):
+    from oracle import attention as A
+    from oracle import mask as omask
+    cores = len(os.sched_getaffinity(0))
+    b, h = 0, 0
+    kvh = h // (cfg.Hq // cfg.Hkv)
+    t0 = time.perf_counter()
+    qn = q[b:b + 1, h:h + 1].double().numpy()
+    kn = k[b:b + 1, kvh:kvh + 1].double().numpy()
+    vn = v[b:b + 1, kvh:kvh + 1].double().numpy()
+    mw = omask.build_mask(1, 1, cfg.S, cfg.S, cfg.tile_m, cfg.tile_n, cfg.tiles_per_bit,
+                          cfg.frac_16bit, cfg.mask_seed, cfg.words_per_row)
+    P = A.make_problem(qn, kn, vn, causal=cfg.causal, code=cfg.code, tile_m=cfg.tile_m,
+                       tile_n=cfg.tile_n, tiles_per_bit=cfg.tiles_per_bit,
+                       frac_16bit=cfg.frac_16bit, seed=cfg.mask_seed, mask_words=mw,
+                       adaptive=cfg.adaptive, exp8=cfg.exp8, tau=cfg.tau, sub_rows=cfg.sub_rows)
+    t_prep = time.perf_counter() - t0
+    flops = 0.0
+    tiles = 0
+    t1 = time.perf_counter()
+    # query tiles from the last (longest) downwards until the budget is spent
+    for qt in range(cfg.n_qt - 1, -1, -1):
+        rows = np.arange(qt * cfg.tile_m, min(cfg.S, (qt + 1) * cfg.tile_m))
+        if A.uses_lamp(P):
+            per = cfg.tile_m // cfg.sub_rows
+            A.attn_lamp(P, 0, 0, np.arange(qt * per, (qt + 1) * per))
+        else:
+            A.attn_tilemix(P, 0, 0, rows)
+        nvalid = int(((np.arange(cfg.S)[None, :] <= rows[:, None]) if cfg.causal
+                      else np.ones((len(rows), cfg.S), bool)).sum())
+        flops += 4.0 * cfg.D * nvalid
+        tiles += 1
+        if time.perf_counter() - t1 > budget_s:
+            break
+    dt = time.perf_counter() - t1
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": (f"numpy fp64 oracle, head (b=0,h=0), {tiles} query tiles of {cfg.tile_m} "
+                       f"rows from the longest down ({tiles * cfg.tile_m} of "
+                       f"{cfg.B * cfg.Hq * cfg.S} query rows of the workload), "
+                       f"{dt:.1f} s; per-head quantisation + mask prep {t_prep:.1f} s excluded"),
+            "seconds": round(dt, 2)}
+
+
+# ---------------------------------------------------------------------------
+# GPU
+# ---------------------------------------------------------------------------
+
+class Pipeline:
+    """Preallocated buffers for one configuration; run() enqueues one step."""
+
+    def __init__(self, L, cfg, qd, kd, vd, torch):
+        self.L, self.cfg, self.torch = L, cfg, torch
+        self.qd, self.kd, self.vd = qd, kd, vd
+        dev = qd.device
+        B, Hq, Hkv, S, D = cfg.B, cfg.Hq, cfg.Hkv, cfg.S, cfg.D
+        self.q8 = torch.empty((B, Hq, S, D), dtype=torch.uint8, device=dev)
+        self.k8 = torch.empty((B, Hkv, S, D), dtype=torch.uint8, device=dev)
+        self.sq = torch.empty((B, Hq, cfg.n_qt), dtype=torch.float32, device=dev)
+        self.sk = torch.empty((B, Hkv, cfg.n_kt), dtype=torch.float32, device=dev)
+        self.mask = torch.empty((B, Hq, cfg.n_qt, cfg.words_per_row), dtype=torch.int64, device=dev)
+        self.out = torch.empty_like(qd)
+        self.flags = None
+        if cfg.adaptive:
+            self.flags = torch.empty(L.lamp.flags_shape(B, Hq, S, S), dtype=torch.int64, device=dev)
+        self.f16 = 0.0 if cfg.mask_all_ones else cfg.frac_16bit
+
+    def prep(self):
+        L, c = self.L, self.cfg
+        L.lamp_quantize_blocks(self.qd, c.tile_m, c.code, codes=self.q8, scales=self.sq)
+        L.lamp_quantize_blocks(self.kd, c.tile_n, c.code, codes=self.k8, scales=self.sk)
+        L.lamp_build_mask(c.B, c.Hq, c.S, c.S, c.tile_m, c.tile_n, c.tiles_per_bit, self.f16,
+                          c.mask_seed, c.words_per_row, mask=self.mask)
+
+    def attn(self):
+        L, c = self.L, self.cfg
+        L.lamp_attn_fwd(self.qd, self.kd, self.vd, self.q8, self.k8, self.sq, self.sk, self.mask,
+                        code=c.code, causal=c.causal, tile_m=c.tile_m,
+                        tiles_per_bit=c.tiles_per_bit, words_per_row=c.words_per_row,
+                        mode=L.LAMP_MODE_ADAPTIVE if c.adaptive else L.LAMP_MODE_MASK,
+                        exp8=c.exp8, tau=c.tau, sub_rows=c.sub_rows, out=self.out,
+                        flags_out=self.flags)
+
+    def counts(self):
+        mw = self.mask.cpu().numpy().view(np.uint64)
+        fl = None if self.flags is None else self.flags.cpu().numpy().view(np.uint64)
+        return route_counts(mw, self.cfg.S, self.cfg.S, self.cfg.tile_m, self.cfg.tile_n,
+                            self.cfg.tiles_per_bit, self.cfg.causal, fl)
+
+
+def time_attn(torch, pipe, iters, warmup):
+    for _ in range(warmup):
+        pipe.attn()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(iters)]
+    for a, b in ev:
+        a.record()
+        pipe.attn()
+        b.record()
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="C5", choices=["C1", "C2", "C3", "C4", "C5"])
+    ap.add_argument("--frac", type=float, default=None, help="C5: 16-bit fraction")
+    ap.add_argument("--code", default=None, choices=["i8", "e4m3"], help="C5: 8-bit code")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the C5 precision-mix sweep")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(each (batch, KV head) group is independent, see the design notes on sharding)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mixed_precision_tiled_amd as L
+    from synthetic import C5_FRACS, get_config, make_inputs
+
+    cfg = get_config(args.config, args.frac, args.code)
+    if args.config == "C5" and args.frac is None and args.code is None:
+        cfg = get_config("C5", 0.25, "i8")
+    dev = torch.device("cuda:0")
+    log(f"[bench] workload {cfg.name}: generating inputs")
+    q, k, v = make_inputs(cfg)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    pipe = Pipeline(L, cfg, qd, kd, vd, torch)
+
+    # ---- warmup, then exactly K timed steps ----
+    for _ in range(args.warmup):
+        pipe.prep()
+        pipe.attn()
+    torch.cuda.synchronize()
+    attn_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(args.steps):
+        pipe.prep()
+        attn_ev[i][0].record()
+        pipe.attn()
+        attn_ev[i][1].record()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_s = t_start.elapsed_time(t_end) * 1e-3 / args.steps
+    attn_s = np.array([a.elapsed_time(b) for a, b in attn_ev]) * 1e-3
+    log(f"[bench] {args.steps} steps: {step_s * 1e3:.3f} ms/step (wall {wall / args.steps * 1e3:.3f}),"
+        f" attention mean {attn_s.mean() * 1e3:.3f} ms min {attn_s.min() * 1e3:.3f}")
+
+    c = pipe.counts()
+    F = algorithmic_flops(c, cfg.D)
+    T_roof = roofline_time(c, cfg.D)
+    attn_mean = float(attn_s.mean())
+    achieved = F / attn_mean / 1e12
+    peak = F / T_roof / 1e12
+    traffic = committed_traffic(cfg.name)
+    result = {
+        "metric": "mixed-precision attn prefill TFLOP/s & % of mix-weighted MFMA roofline",
+        "value": round(F / step_s / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": ("i8" if cfg.code == "i8" else "e4m3") + "+bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.B, "q_heads": cfg.Hq, "kv_heads": cfg.Hkv,
+                   "seq_len": cfg.S, "head_dim": cfg.D, "causal": cfg.causal,
+                   "tile_m": cfg.tile_m, "tile_n": cfg.tile_n,
+                   "tiles_per_bit": cfg.tiles_per_bit, "frac_16bit": cfg.frac_16bit,
+                   "code": cfg.code, "exp8": cfg.exp8, "adaptive": cfg.adaptive,
+                   "input_dtype": cfg.dtype},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 2),
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic,
+                     "kernel": "attn_fwd_kernel", "attn_ms_mean": round(attn_mean * 1e3, 4),
+                     "attn_ms_min": round(float(attn_s.min()) * 1e3, 4),
+                     "t_roof_ms": round(T_roof * 1e3, 4),
+                     "counts": c, "fa_convention_tflops": round(cfg.fa_flops() / attn_mean / 1e12, 2),
+                     "peaks": {"int8_fp8": PEAK8, "bf16_fp16": PEAK16},
+                     "kernel_source_sha256": kernel_source_hash()},
+    }
+    if args.config == "C5" and not args.no_sweep:
+        sweep = {}
+        for code in ("i8", "e4m3"):
+            for f in C5_FRACS:
+                sc = get_config("C5", f, code)
+                sp = Pipeline(L, sc, qd, kd, vd, torch)
+                sp.prep()
+                ts = time_attn(torch, sp, iters=5, warmup=1)
+                cc = sp.counts()
+                tr = roofline_time(cc, sc.D)
+                sweep[f"{code}_f{int(round(100 * f)):02d}"] = {
+                    "attn_ms": round(float(np.median(ts)) * 1e3, 4),
+                    "tflops": round(algorithmic_flops(cc, sc.D) / float(np.median(ts)) / 1e12, 1),
+                    "roofline_frac": round(tr / float(np.median(ts)), 4),
+                    "t_roof_ms": round(tr * 1e3, 4)}
+                del sp
+        result["sweep_c5_attention"] = sweep
+        log(f"[bench] sweep {json.dumps(sweep)}")
+    if not args.no_cpu:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(cfg, q, k, v, budget_s=args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,200 @@
+/*
+ * lamp.h -- C ABI of the mixed-precision tiled attention prefill library
+ * (HIP, gfx950 / MI355X).
+ *
+ * The library computes a FlashAttention-style prefill forward pass in which
+ * every QK^T score tile takes one of two paths, both feeding one shared
+ * online-softmax state (running maximum m, normaliser l, accumulator O):
+ *
+ *   8-bit path  Q and K quantised per block (int8 or OCP e4m3) with one fp32
+ *               scale per block; 8-bit MFMA; logits rescaled by
+ *               sQ * sK * sm_scale; optionally the max-shifted logit and its
+ *               exponential rounded to e4m3 ("exp8").
+ *   16-bit path Q and K in bf16/fp16; 16-bit MFMA.
+ *
+ * Sources (pages, by title and section):
+ *   - "TileMix: Mixed-Precision Attention for Faster LLM Prefill",
+ *     section 2: score tiles (The Tile Architecture), packed per-query-row
+ *     bitmask with one bit per group of key tiles, 0 = 16-bit, 1 = 8-bit
+ *     (Packed Bitmasks), in-loop dispatch and per-block scale factors
+ *     feeding a shared online-softmax state (The Dual-Path Engine);
+ *     section 4: grouped-query attention.
+ *   - "LampAttention: Look-Ahead Mixed-Precision FlashAttention for Dedicated
+ *     Accelerators", Abstract: 8-bit products and exponentials, adaptive
+ *     identification of sensitive sub-blocks and their 16-bit recompute.
+ *
+ * Conventions for every entry point:
+ *   - Every data pointer is a DEVICE pointer owned by the caller.  The
+ *     library allocates no memory, keeps no state other than a thread-local
+ *     error string, never synchronises, and enqueues its kernels on `stream`
+ *     (a hipStream_t; NULL = the null stream).
+ *   - Arguments are validated synchronously on the host before anything is
+ *     launched; on error nothing is enqueued and the call returns a non-zero
+ *     lamp_status whose detail is in lamp_last_error().
+ *   - Device faults surface at the caller's next synchronisation.
+ *   - Sizes are element counts; strides are in elements; the innermost (head
+ *     dim) stride is 1.
+ *   - A call with an empty problem (any of B, H, S equal to 0) validates its
+ *     arguments and returns LAMP_OK without launching.
+ */
+#ifndef LAMP_H_
+#define LAMP_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LAMP_ABI_VERSION 1
+
+typedef enum {
+  LAMP_OK = 0,
+  LAMP_ERR_NULL = 1,        /* a required pointer is NULL                      */
+  LAMP_ERR_SHAPE = 2,       /* negative / inconsistent sizes or strides        */
+  LAMP_ERR_UNSUPPORTED = 3, /* a valid request this build does not implement   */
+  LAMP_ERR_ALIGN = 4,       /* pointer or row stride not 16-byte aligned       */
+  LAMP_ERR_HIP = 5          /* the HIP runtime refused a launch                */
+} lamp_status;
+
+typedef enum { LAMP_F16 = 0, LAMP_BF16 = 1, LAMP_I8 = 2, LAMP_E4M3 = 3 } lamp_dtype;
+
+typedef enum {
+  LAMP_MODE_MASK = 0,       /* TileMix: route by the packed mask only          */
+  LAMP_MODE_ADAPTIVE = 1    /* LampAttention: mask, then look-ahead flags      */
+} lamp_mode;
+
+/*
+ * lamp_quantize_blocks -- per-block absmax quantisation of Q or K.
+ *
+ * Source: TileMix page, section 2 "The Dual-Path Engine" (queries and keys
+ * quantised, products rescaled with per-block scale factors); LampAttention
+ * abstract (8-bit floating-point format).
+ *
+ * x       [B, H, S, D] 16-bit (x_dtype LAMP_F16 or LAMP_BF16) at element
+ *         strides (sb, sh, ss, 1); 16-byte aligned, ss a multiple of 8.
+ * block   `block_rows` consecutive rows of one (b, h) times all D columns
+ *         (use tile_m for Q and tile_n for K); the last block of a sequence
+ *         may be short.  1 <= block_rows <= 256.
+ * scale   a = max |x| over the block; a == 0 gives scale 0 and all codes 0;
+ *         otherwise, in fp32 with round-to-nearest-even,
+ *           scale = a / QMAX, inv = QMAX / a, y = x * inv,
+ *         QMAX = 127 (LAMP_I8) or 448 (LAMP_E4M3).
+ * codes   [B, H, S, D] contiguous, one byte each, 16-byte aligned:
+ *           LAMP_I8:   clamp(round_half_even(y), -127, 127) (two's complement)
+ *           LAMP_E4M3: OCP E4M3FN bits of y, round-half-even, |y| <= 448.
+ * scales  [B, H, ceil(S / block_rows)] fp32 contiguous.
+ * D       64, 128 or 256.
+ */
+lamp_status lamp_quantize_blocks(const void* x, int32_t x_dtype, int64_t B, int64_t H,
+                                 int64_t S, int64_t D, int64_t sb, int64_t sh, int64_t ss,
+                                 int32_t block_rows, int32_t code_dtype, void* codes,
+                                 float* scales, void* stream);
+
+/*
+ * lamp_build_mask -- the random packed precision mask.
+ *
+ * Source: TileMix page, section 2 "Packed Bitmasks".  One mask row per query
+ * tile of tile_m rows; group g covers key tiles [g*G, (g+1)*G) with
+ * G = tiles_per_bit, n_g = ceil(ceil(S_k / tile_n) / G) groups; the row is
+ * `words_per_row` uint64 words, bit g % 64 of word g / 64 (LSB first), bit 1
+ * = 8-bit path, 0 = 16-bit path, unused bits 0.
+ *
+ * Template: every (b, h, qt, g) is drawn independently.  r = output number
+ * ((b*Hq + h)*n_qt + qt)*n_g + g of SplitMix64 (Steele, Lea & Flood 2014)
+ * seeded with `seed`; the group is 16-bit iff (r >> 32) < floor(frac_16bit *
+ * 2^32).  frac_16bit in [0, 1].
+ *
+ * mask    [B, Hq, ceil(S_q / tile_m), words_per_row] uint64, 8-byte aligned;
+ *         words_per_row >= ceil(n_g / 64).
+ */
+lamp_status lamp_build_mask(int64_t B, int64_t Hq, int64_t S_q, int64_t S_k, int32_t tile_m,
+                            int32_t tile_n, int32_t tiles_per_bit, double frac_16bit,
+                            uint64_t seed, uint64_t* mask, int32_t words_per_row,
+                            void* stream);
+
+/*
+ * lamp_attn_fwd -- the dual-path fused attention forward.
+ *
+ * Sources: TileMix page, section 2 (tile loop, per-group dispatch, shared
+ * online softmax) and section 4 (grouped-query attention); LampAttention
+ * abstract (8-bit exponentials, adaptive sub-block recompute in 16 bits).
+ *
+ * For query row i of head h (KV head h / (Hq / Hkv)) and key j:
+ *   valid(i, j)  = j < S_k, and j <= i when causal (then S_q == S_k);
+ *   route8(i, j) = mask bit of (b, h, i / tile_m, (j / tile_n) / G);
+ *   s16 = sm * q_i . k_j            s8 = (cq_i . ck_j) * sQ * sK * sm.
+ * MODE_MASK, exp8 = 0: O_i = softmax over valid j of the routed logits, times V.
+ * Otherwise key tiles are processed in ascending order with the state
+ * (m, l, acc) updated after each tile of tile_n = 64 keys:
+ *   - ADAPTIVE, 8-bit-routed tile: m' = max(m, rowmax s8); the sub-block of
+ *     sub_rows = 32 rows is flagged iff some valid s8_ij - m'_i >= -tau, and
+ *     then uses s16 for all its elements in this tile;
+ *   - m_new = max(m, rowmax s); alpha = exp(m - m_new);
+ *   - p = exp(s - m_new) on 16-bit elements; on 8-bit elements
+ *     p = e4m3(exp(e4m3(max(s - m_new, -448)))) when exp8, else exp(s - m_new);
+ *   - l = alpha*l + sum p;  acc = alpha*acc + p V;  O = acc / l at the end.
+ * V is never quantised; P V runs at 16 bits on both paths.
+ *
+ * Supported: D in {64, 128, 256}; tile_m in {64, 128}; tile_n == 64;
+ * in_dtype LAMP_F16 or LAMP_BF16 (q, k, v, out share it); code_dtype LAMP_I8
+ * or LAMP_E4M3; sub_rows == 32 in ADAPTIVE mode; Hq % Hkv == 0.
+ *
+ * Pointers (device): q/k/v/out 16-byte aligned with row strides multiple of
+ * 8 elements; q8 [B, Hq, S_q, D] and k8 [B, Hkv, S_k, D] contiguous codes
+ * and q_scale [B, Hq, ceil(S_q/tile_m)], k_scale [B, Hkv, ceil(S_k/64)] as
+ * written by lamp_quantize_blocks (block_rows tile_m and 64); mask as
+ * written by lamp_build_mask.
+ * Optional outputs (NULL = not written):
+ *   lse        [B, Hq, S_q] fp32, natural-log sum exp of the logits;
+ *   flags_out  [B, Hq, ceil(S_q/32), ceil(ceil(S_k/64)/64)] uint64, ADAPTIVE:
+ *              bit kt % 64 of word kt / 64 set iff the sub-block was flagged
+ *              at key tile kt (all other bits 0);
+ *   dbg_qk_acc [B, Hq, S_q, S_k] int32, int8 path only: the raw int32 QK^T
+ *              accumulators of every 8-bit key tile a 32-row wave computes
+ *              (tiny shapes; other entries are left untouched).
+ */
+typedef struct {
+  uint32_t struct_size;     /* = sizeof(lamp_attn_params); ABI guard         */
+  int32_t mode;             /* lamp_mode                                     */
+  int32_t causal;           /* 0 / 1                                         */
+  float sm_scale;           /* <= 0 selects 1/sqrt(D)                        */
+  int64_t B, Hq, Hkv, S_q, S_k, D;
+  const void* q;            /* [B, Hq, S_q, D]                               */
+  const void* k;            /* [B, Hkv, S_k, D]                              */
+  const void* v;            /* [B, Hkv, S_k, D]                              */
+  int32_t in_dtype;         /* lamp_dtype: LAMP_F16 | LAMP_BF16              */
+  int32_t code_dtype;       /* lamp_dtype: LAMP_I8 | LAMP_E4M3               */
+  int64_t q_str[3], k_str[3], v_str[3], o_str[3]; /* (batch, head, row)      */
+  const void* q8;
+  const void* k8;
+  const float* q_scale;
+  const float* k_scale;
+  const uint64_t* mask;
+  int32_t words_per_row;
+  int32_t tile_m, tile_n, tiles_per_bit;
+  int32_t exp8;             /* 1: 8-bit logit and exp on the 8-bit path      */
+  float tau;                /* ADAPTIVE threshold (natural-log units)        */
+  int32_t sub_rows;         /* ADAPTIVE sub-block rows (32)                  */
+  void* out;                /* [B, Hq, S_q, D] in_dtype                      */
+  float* lse;               /* optional                                      */
+  uint64_t* flags_out;      /* optional, ADAPTIVE                            */
+  int32_t* dbg_qk_acc;      /* optional, int8 path                           */
+} lamp_attn_params;
+
+lamp_status lamp_attn_fwd(const lamp_attn_params* p, void* stream);
+
+/* Static name of a status code. */
+const char* lamp_status_string(lamp_status s);
+
+/* Detail of the last failing call on this thread ("" if none). */
+const char* lamp_last_error(void);
+
+/* LAMP_ABI_VERSION of the built library. */
+int32_t lamp_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LAMP_H_ */

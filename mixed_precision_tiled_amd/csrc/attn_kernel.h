@@ -1,0 +1,497 @@
+// Dual-path (8-bit / 16-bit) fused attention prefill forward for gfx950.
+//
+// Sources (pages, by title and section):
+//   "TileMix: Mixed-Precision Attention for Faster LLM Prefill", section 2:
+//     the score matrix is processed one hardware-aligned tile at a time; the
+//     inner loop reads the packed mask bit of the current key-tile group and
+//     dispatches the tile's QK^T to a 16-bit product or to an INT8 product
+//     rescaled with per-block scales; both update one shared online-softmax
+//     state.  Section 4: grouped-query attention.
+//   "LampAttention: Look-Ahead Mixed-Precision FlashAttention for Dedicated
+//     Accelerators", Abstract: 8-bit products and exponentials, sensitive
+//     sub-blocks found adaptively and recomputed in 16 bits.
+//
+// MI355X design (not the pages' A100 / accelerator design):
+//   * one workgroup = one query tile of TM = 32*NW rows of one (b, h); each
+//     64-lane wave owns 32 query rows;
+//   * a wave computes S^T = K Q^T with 32x32 MFMAs (A = K from LDS, B = Q held
+//     in registers), so lane l ends up with the 32 logits of query row l%32
+//     for its half of the 64-key tile: the row max / row sum need a single
+//     cross-half exchange, and alpha rescales only the lane's own rows;
+//   * P V is computed as O^T = V^T P^T: the S^T accumulator registers are, once
+//     converted to 16 bits, exactly the B operand of the next MFMA (no LDS
+//     round trip for P); V is staged in LDS transposed (d-major) with the key
+//     order inside each 16-key group permuted to match that register layout;
+//   * K (as K16 or K8, whichever the mask selects) and V are double-buffered
+//     in LDS through registers, one barrier per key tile;
+//   * workgroups are mapped so that each XCD processes whole KV-head groups
+//     (shared K/V in its L2), longest causal query tiles first.
+#pragma once
+
+#include "lamp_device.h"
+#include "lamp_internal.h"
+
+namespace lamp {
+
+template <int D, int NW>
+struct AttnShape {
+  static constexpr int TM = NW * 32;            // query rows per workgroup
+  static constexpr int TN = 64;                 // keys per tile
+  static constexpr int NT = NW * 64;            // threads
+  static constexpr int ND = D / 32;             // O^T blocks of 32 head-dim rows
+  static constexpr int NQ16 = D / 16;           // 16-bit MFMAs per 32-key block
+  static constexpr int NQ8 = D / 32;            // 16-byte Q8 fragments per lane
+  static constexpr int K16_BYTES = TN * D * 2;
+  static constexpr int V_BYTES = TN * D * 2;
+  static constexpr int STAGE = K16_BYTES + V_BYTES;
+  static constexpr int CH16 = D / 8;            // 16-byte chunks per K16 row
+  static constexpr int CH8 = D / 16;            // 16-byte chunks per K8 row
+  static constexpr int M16 = (CH16 < 16 ? CH16 : 16) - 1;   // XOR swizzle masks
+  static constexpr int M8 = (CH8 < 16 ? CH8 : 16) - 1;
+  static constexpr int N_K16 = TN * CH16;       // 16-byte loads per tile
+  static constexpr int N_K8 = TN * CH8;
+  static constexpr int N_V = (TN / 4) * (D / 8);   // 4-key x 8-dim blocks per tile
+  static constexpr int LD_K16 = (N_K16 + NT - 1) / NT;
+  static constexpr int LD_K8 = (N_K8 + NT - 1) / NT;
+  static constexpr int LD_V = (N_V + NT - 1) / NT;
+};
+
+// LDS byte offset of 16-byte chunk `ch` of K row `r` (row length rowbytes).
+template <int MASK>
+__device__ __forceinline__ int k_off(int r, int ch, int rowbytes) {
+  return r * rowbytes + ((ch ^ (r & MASK)) << 4);
+}
+// LDS byte offset of 16-byte chunk `ch` (0..7) of V^T row d (128 bytes/row).
+__device__ __forceinline__ int vt_off(int d, int ch) {
+  return d * 128 + ((ch ^ ((d ^ (d >> 3)) & 7)) << 4);
+}
+
+template <int D, int NW, bool BF16, bool E4M3, bool ADAPTIVE, bool EXP8>
+__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
+  using SH = AttnShape<D, NW>;
+  // lazy rescale with base-2 logits is exact in exact arithmetic and is used
+  // whenever no 8-bit rounding or flag decision depends on the running max
+  constexpr bool LAZY = !ADAPTIVE && !EXP8;
+  __shared__ __attribute__((aligned(16))) char smem[2 * SH::STAGE];
+
+  // ---- workgroup -> (b, h, qt): XCD-contiguous chunks of the logical order
+  //      (b, kv-head group) major, query tile descending, head minor ----
+  const int nblk = (int)gridDim.x, bid = (int)blockIdx.x;
+  const int xcd = bid & 7, slot = bid >> 3, qn = nblk >> 3, rn = nblk & 7;
+  const int lin = xcd * qn + min(xcd, rn) + slot;
+  const int per_group = a.n_qt * a.heads_per_group;
+  const int grp = lin / per_group;
+  const int rem = lin - grp * per_group;
+  const int qt = a.n_qt - 1 - rem / a.heads_per_group;
+  const int hh = rem % a.heads_per_group;
+  const int b = grp / a.Hkv, kvh = grp % a.Hkv;
+  const int h = kvh * a.heads_per_group + hh;
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int lr = lane & 31, hf = lane >> 5;
+  const int row0 = qt * SH::TM + w * 32;
+  const int my_row = row0 + lr;
+  const bool wave_live = row0 < a.S_q;
+  const int q_row = min(my_row, a.S_q - 1);
+
+  const int wg_last = min(a.S_q, (qt + 1) * SH::TM) - 1;
+  const int kt_end = a.causal ? min(a.n_kt, wg_last / 64 + 1) : a.n_kt;
+  const int w_last = min(a.S_q, row0 + 32) - 1;
+  const int kt_end_w = !wave_live ? 0 : (a.causal ? min(a.n_kt, w_last / 64 + 1) : a.n_kt);
+  const bool rows_ragged = row0 + 32 > a.S_q;
+
+  // ---- Q fragments (B operand of S^T = K Q^T), resident for the whole loop
+  const char* qp = reinterpret_cast<const char*>(a.q) +
+                   2 * (b * a.q_sb + h * a.q_sh + (int64_t)q_row * a.q_ss);
+  u32x4 q16[SH::NQ16];
+#pragma unroll
+  for (int t = 0; t < SH::NQ16; ++t) q16[t] = ld_global16(qp + 2 * (16 * t + 8 * hf));
+  const uint8_t* q8p = a.q8 + (((int64_t)b * a.Hq + h) * a.S_q + q_row) * D;
+  u32x4 q8[SH::NQ8];
+  if constexpr (E4M3) {
+#pragma unroll
+    for (int t = 0; t < D / 64; ++t) {
+      q8[2 * t] = ld_global16(q8p + 64 * t + 32 * hf);
+      q8[2 * t + 1] = ld_global16(q8p + 64 * t + 32 * hf + 16);
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) q8[t] = ld_global16(q8p + 32 * t + 16 * hf);
+  }
+  const float sQ = a.q_scale[((int64_t)b * a.Hq + h) * a.n_qt + qt];
+  const uint64_t* mrow = a.mask + (((int64_t)b * a.Hq + h) * a.n_qt + qt) * a.words_per_row;
+
+  const char* kp = reinterpret_cast<const char*>(a.k) + 2 * (b * a.k_sb + kvh * a.k_sh);
+  const char* vp = reinterpret_cast<const char*>(a.v) + 2 * (b * a.v_sb + kvh * a.v_sh);
+  const uint8_t* k8p = a.k8 + ((int64_t)b * a.Hkv + kvh) * a.S_k * D;
+  const float* sKp = a.k_scale + ((int64_t)b * a.Hkv + kvh) * a.n_kt;
+
+  auto tile_is8 = [&](int kt) -> bool {
+    const int g = kt / a.tiles_per_bit;
+    return (mrow[g >> 6] >> (g & 63)) & 1ull;
+  };
+
+  // ---- global -> register staging of one key tile ----
+  u32x4 kst[SH::LD_K16];
+  u32x4 vst[4 * SH::LD_V];
+  auto load_tile = [&](int kt, bool is8) {
+    const int key0 = kt * SH::TN;
+    if (is8) {
+#pragma unroll
+      for (int i = 0; i < SH::LD_K8; ++i) {
+        const int c = tid + i * SH::NT;
+        if (SH::N_K8 % SH::NT == 0 || c < SH::N_K8) {
+          const int r = c / SH::CH8, ch = c % SH::CH8;
+          const int key = min(key0 + r, a.S_k - 1);
+          kst[i] = ld_global16(k8p + (int64_t)key * D + ch * 16);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < SH::LD_K16; ++i) {
+        const int c = tid + i * SH::NT;
+        if (SH::N_K16 % SH::NT == 0 || c < SH::N_K16) {
+          const int r = c / SH::CH16, ch = c % SH::CH16;
+          const int key = min(key0 + r, a.S_k - 1);
+          kst[i] = ld_global16(kp + 2 * ((int64_t)key * a.k_ss + ch * 8));
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < SH::LD_V; ++i) {
+      const int bi = tid + i * SH::NT;
+      if (SH::N_V % SH::NT == 0 || bi < SH::N_V) {
+        const int dc = bi % (D / 8), kg = bi / (D / 8);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = min(key0 + 4 * kg + r, a.S_k - 1);
+          vst[4 * i + r] = ld_global16(vp + 2 * ((int64_t)key * a.v_ss + dc * 8));
+        }
+      }
+    }
+  };
+  auto store_tile = [&](int buf, bool is8) {
+    char* kb = smem + buf * SH::STAGE;
+    char* vb = kb + SH::K16_BYTES;
+    if (is8) {
+#pragma unroll
+      for (int i = 0; i < SH::LD_K8; ++i) {
+        const int c = tid + i * SH::NT;
+        if (SH::N_K8 % SH::NT == 0 || c < SH::N_K8) {
+          const int r = c / SH::CH8, ch = c % SH::CH8;
+          st_lds16(kb + k_off<SH::M8>(r, ch, D), kst[i]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < SH::LD_K16; ++i) {
+        const int c = tid + i * SH::NT;
+        if (SH::N_K16 % SH::NT == 0 || c < SH::N_K16) {
+          const int r = c / SH::CH16, ch = c % SH::CH16;
+          st_lds16(kb + k_off<SH::M16>(r, ch, 2 * D), kst[i]);
+        }
+      }
+    }
+    // V: 4 keys x 8 dims per block, transposed to 8 dims x 4 keys; within a
+    // 16-key group the 4-key runs are stored in the order 0, 2, 1, 3 so that
+    // one 16-byte LDS chunk holds keys {4h..4h+3, 8+4h..8+4h+3} for h = 0, 1
+#pragma unroll
+    for (int i = 0; i < SH::LD_V; ++i) {
+      const int bi = tid + i * SH::NT;
+      if (SH::N_V % SH::NT == 0 || bi < SH::N_V) {
+        const int dc = bi % (D / 8), kg = bi / (D / 8);
+        const int g16 = kg >> 2, qq = kg & 3;
+        const int ch = 2 * g16 + (qq & 1), half = qq >> 1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int d = 8 * dc + e;
+          const int we = e >> 1;
+          uint32_t lo, hi;
+          if (e & 1) {
+            lo = (vst[4 * i + 0][we] >> 16) | (vst[4 * i + 1][we] & 0xFFFF0000u);
+            hi = (vst[4 * i + 2][we] >> 16) | (vst[4 * i + 3][we] & 0xFFFF0000u);
+          } else {
+            lo = (vst[4 * i + 0][we] & 0xFFFFu) | (vst[4 * i + 1][we] << 16);
+            hi = (vst[4 * i + 2][we] & 0xFFFFu) | (vst[4 * i + 3][we] << 16);
+          }
+          st_lds8(vb + vt_off(d, ch) + 8 * half, u32x2{lo, hi});
+        }
+      }
+    }
+  };
+
+  // ---- online-softmax state of row my_row (lane-local; the two lane halves
+  //      hold partial sums of l that are combined at the end) ----
+  f32x16 O[SH::ND];
+#pragma unroll
+  for (int db = 0; db < SH::ND; ++db) O[db] = f32x16{};
+  float m_run = kNegInf;
+  float l_run = 0.f;
+  uint64_t fword = 0;
+
+  const int sb_index = qt * NW + w;      // 32-row sub-block of this wave
+  uint64_t* frow = (ADAPTIVE && a.flags != nullptr && wave_live)
+                       ? a.flags + (((int64_t)b * a.Hq + h) * a.n_sb + sb_index) * a.flag_words
+                       : nullptr;
+
+  auto compute_tile = [&](int kt, int buf, bool is8) {
+    const char* kb = smem + buf * SH::STAGE;
+    const char* vb = kb + SH::K16_BYTES;
+    const int key0 = kt * SH::TN;
+    const bool need_mask = rows_ragged || (key0 + SH::TN > a.S_k) ||
+                           (a.causal && key0 + SH::TN - 1 > row0);
+    float s[32];
+    bool is16 = !is8;
+
+    auto apply_mask = [&]() {
+      if (need_mask) {
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+          const int kb_ = e >> 4, i = e & 15;
+          const int j = key0 + kb_ * 32 + (i >> 2) * 8 + hf * 4 + (i & 3);
+          const bool ok = j < a.S_k && my_row < a.S_q && (!a.causal || j <= my_row);
+          s[e] = ok ? s[e] : kNegInf;
+        }
+      }
+    };
+    auto qk16_from_lds = [&](float scale) {
+#pragma unroll
+      for (int kb_ = 0; kb_ < 2; ++kb_) {
+        f32x16 acc = f32x16{};
+        const int r = kb_ * 32 + lr;
+#pragma unroll
+        for (int t = 0; t < SH::NQ16; ++t) {
+          const u32x4 af = ld_lds16(kb + k_off<SH::M16>(r, 2 * t + hf, 2 * D));
+          acc = mfma16<BF16>(af, q16[t], acc);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[kb_ * 16 + i] = acc[i] * scale;
+      }
+    };
+
+    const float sm = a.sm_scale;
+    if (is8) {
+      const float c8 = (sQ * sKp[kt]) * sm;
+      const float sc = LAZY ? c8 * kLog2e : c8;
+#pragma unroll
+      for (int kb_ = 0; kb_ < 2; ++kb_) {
+        const int r = kb_ * 32 + lr;
+        if constexpr (E4M3) {
+          f32x16 acc = f32x16{};
+#pragma unroll
+          for (int t = 0; t < D / 64; ++t) {
+            const u32x4 a0 = ld_lds16(kb + k_off<SH::M8>(r, 4 * t + 2 * hf, D));
+            const u32x4 a1 = ld_lds16(kb + k_off<SH::M8>(r, 4 * t + 2 * hf + 1, D));
+            acc = mfma_e4m3(a0, a1, q8[2 * t], q8[2 * t + 1], acc);
+          }
+#pragma unroll
+          for (int i = 0; i < 16; ++i) s[kb_ * 16 + i] = acc[i] * sc;
+        } else {
+          i32x16 acc = i32x16{};
+#pragma unroll
+          for (int t = 0; t < D / 32; ++t) {
+            const u32x4 af = ld_lds16(kb + k_off<SH::M8>(r, 2 * t + hf, D));
+            acc = mfma_i8(af, q8[t], acc);
+          }
+          if (a.dbg != nullptr && my_row < a.S_q) {
+            int32_t* dr = a.dbg + (((int64_t)b * a.Hq + h) * a.S_q + my_row) * a.S_k;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int j = key0 + kb_ * 32 + (i >> 2) * 8 + hf * 4 + (i & 3);
+              if (j < a.S_k) dr[j] = acc[i];
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < 16; ++i) s[kb_ * 16 + i] = (float)acc[i] * sc;
+        }
+      }
+      apply_mask();
+      if constexpr (ADAPTIVE) {
+        // look-ahead: m' = max(m, rowmax s8); flag the 32-row sub-block if
+        // some valid 8-bit logit is within tau of m'
+        float mx8 = s[0];
+#pragma unroll
+        for (int e = 1; e < 32; ++e) mx8 = fmaxf(mx8, s[e]);
+        mx8 = fmaxf(mx8, wave_swap32(mx8));
+        const float mprime = fmaxf(m_run, mx8);
+        const bool cond = (mx8 != kNegInf) && (mx8 - mprime >= -a.tau);
+        if (wave_any(cond)) {
+          is16 = true;
+          fword |= 1ull << (kt & 63);
+          // recompute the sub-block's logits at 16 bits, K16 straight from
+          // global memory (only flagged sub-blocks need it)
+#pragma unroll
+          for (int kb_ = 0; kb_ < 2; ++kb_) {
+            f32x16 acc = f32x16{};
+            const int key = min(key0 + kb_ * 32 + lr, a.S_k - 1);
+            const char* kr = kp + 2 * ((int64_t)key * a.k_ss);
+#pragma unroll
+            for (int t = 0; t < SH::NQ16; ++t) {
+              const u32x4 af = ld_global16(kr + 2 * (16 * t + 8 * hf));
+              acc = mfma16<BF16>(af, q16[t], acc);
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[kb_ * 16 + i] = acc[i] * sm;
+          }
+          apply_mask();
+        }
+      }
+    } else {
+      qk16_from_lds(LAZY ? sm * kLog2e : sm);
+      apply_mask();
+    }
+
+    // ---- shared online-softmax update ----
+    float mx = s[0];
+#pragma unroll
+    for (int e = 1; e < 32; ++e) mx = fmaxf(mx, s[e]);
+    mx = fmaxf(mx, wave_swap32(mx));
+    float p[32];
+    if constexpr (LAZY) {
+      // base-2 logits; the reference max only moves when a row's max grows
+      // by more than 8 (p <= 2^8 in between), which changes no result in
+      // exact arithmetic
+      if (wave_any(mx > m_run + 8.f)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = (m_new == kNegInf) ? 1.f : exp2_fast(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < SH::ND; ++db) O[db] *= alpha;
+        m_run = m_new;
+      }
+      const float msub = (m_run == kNegInf) ? 0.f : m_run;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) p[e] = exp2_fast(s[e] - msub);
+    } else {
+      const float m_new = fmaxf(m_run, mx);
+      if (wave_any(m_new != m_run)) {
+        const float alpha = (m_run == kNegInf) ? 0.f : exp2_fast((m_run - m_new) * kLog2e);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < SH::ND; ++db) O[db] *= alpha;
+        m_run = m_new;
+      }
+      const float msub = (m_run == kNegInf) ? 0.f : m_run;
+      if (EXP8 && !is16) {
+        // x = s - m rounded to e4m3, exp, rounded to e4m3 again
+#pragma unroll
+        for (int e = 0; e < 32; e += 2) {
+          const float x0 = fmaxf(s[e] - msub, -448.f);
+          const float x1 = fmaxf(s[e + 1] - msub, -448.f);
+          const f32x2 xq = e4m3x2_to_f32(f32x2_to_e4m3(x0, x1));
+          const float e0 = exp2_fast(xq.x * kLog2e);
+          const float e1 = exp2_fast(xq.y * kLog2e);
+          const f32x2 pq = e4m3x2_to_f32(f32x2_to_e4m3(e0, e1));
+          p[e] = pq.x;
+          p[e + 1] = pq.y;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 32; ++e) p[e] = exp2_fast((s[e] - msub) * kLog2e);
+      }
+    }
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) psum += p[e];
+    l_run += psum;
+
+    // ---- O^T += V^T P^T ----
+#pragma unroll
+    for (int kb_ = 0; kb_ < 2; ++kb_) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int e0 = kb_ * 16 + 8 * c;
+        const u32x4 pb = {pack16x2<BF16>(p[e0], p[e0 + 1]), pack16x2<BF16>(p[e0 + 2], p[e0 + 3]),
+                          pack16x2<BF16>(p[e0 + 4], p[e0 + 5]), pack16x2<BF16>(p[e0 + 6], p[e0 + 7])};
+        const int ch = 4 * kb_ + 2 * c + hf;
+#pragma unroll
+        for (int db = 0; db < SH::ND; ++db) {
+          const u32x4 vf = ld_lds16(vb + vt_off(db * 32 + lr, ch));
+          O[db] = mfma16<BF16>(vf, pb, O[db]);
+        }
+      }
+    }
+  };
+
+  // ---- main loop over key tiles, ascending ----
+  bool is8_cur = tile_is8(0);
+  load_tile(0, is8_cur);
+  store_tile(0, is8_cur);
+  __syncthreads();
+  for (int kt = 0; kt < kt_end; ++kt) {
+    const int buf = kt & 1;
+    bool is8_next = false;
+    const bool has_next = kt + 1 < kt_end;
+    if (has_next) {
+      is8_next = tile_is8(kt + 1);
+      load_tile(kt + 1, is8_next);
+    }
+    if (kt < kt_end_w) compute_tile(kt, buf, is8_cur);
+    if (has_next) store_tile(buf ^ 1, is8_next);
+    if constexpr (ADAPTIVE) {
+      if (((kt & 63) == 63) || kt == kt_end - 1) {
+        if (frow != nullptr && lane == 0) frow[kt >> 6] = fword;
+        fword = 0;
+      }
+    }
+    __syncthreads();
+    is8_cur = is8_next;
+  }
+  if constexpr (ADAPTIVE) {
+    if (frow != nullptr && lane == 0) {
+      for (int wd = ((kt_end - 1) >> 6) + 1; wd < a.flag_words; ++wd) frow[wd] = 0;
+    }
+  }
+
+  // ---- epilogue: O = acc / l, 16-bit store, optional LSE ----
+  const float l_tot = l_run + wave_swap32(l_run);
+  if (wave_live && my_row < a.S_q) {
+    const float inv_l = 1.f / l_tot;
+    char* op = reinterpret_cast<char*>(a.out) +
+               2 * (b * a.o_sb + h * a.o_sh + (int64_t)my_row * a.o_ss);
+#pragma unroll
+    for (int db = 0; db < SH::ND; ++db) {
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int d0 = db * 32 + ii * 8 + hf * 4;
+        const u32x2 v2 = {pack16x2<BF16>(O[db][4 * ii] * inv_l, O[db][4 * ii + 1] * inv_l),
+                          pack16x2<BF16>(O[db][4 * ii + 2] * inv_l, O[db][4 * ii + 3] * inv_l)};
+        *reinterpret_cast<u32x2*>(op + 2 * d0) = v2;
+      }
+    }
+    if (a.lse != nullptr && hf == 0) {
+      const float lg = __builtin_amdgcn_logf(l_tot);      // log2
+      const float lse = LAZY ? (m_run + lg) * kLn2 : m_run + lg * kLn2;
+      a.lse[((int64_t)b * a.Hq + h) * a.S_q + my_row] = lse;
+    }
+  }
+}
+
+template <int D, int NW, bool BF16, bool E4M3, bool AD, bool X8>
+hipError_t launch_attn_one(const AttnArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)((int64_t)a.B * a.Hq * a.n_qt));
+  const dim3 block(NW * 64);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, NW, BF16, E4M3, AD, X8>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D, int NW, bool BF16, bool E4M3, bool AD>
+hipError_t dispatch_x8(const AttnArgs& a, const AttnConfig& c, hipStream_t s) {
+  return c.exp8 ? launch_attn_one<D, NW, BF16, E4M3, AD, true>(a, s)
+                : launch_attn_one<D, NW, BF16, E4M3, AD, false>(a, s);
+}
+template <int D, int NW, bool BF16, bool E4M3>
+hipError_t dispatch_ad(const AttnArgs& a, const AttnConfig& c, hipStream_t s) {
+  return c.adaptive ? dispatch_x8<D, NW, BF16, E4M3, true>(a, c, s)
+                    : dispatch_x8<D, NW, BF16, E4M3, false>(a, c, s);
+}
+template <int D, int NW, bool BF16>
+hipError_t dispatch_code(const AttnArgs& a, const AttnConfig& c, hipStream_t s) {
+  return c.e4m3 ? dispatch_ad<D, NW, BF16, true>(a, c, s) : dispatch_ad<D, NW, BF16, false>(a, c, s);
+}
+template <int D, int NW>
+hipError_t dispatch_dtype(const AttnArgs& a, const AttnConfig& c, hipStream_t s) {
+  return c.bf16 ? dispatch_code<D, NW, true>(a, c, s) : dispatch_code<D, NW, false>(a, c, s);
+}
+
+}  // namespace lamp

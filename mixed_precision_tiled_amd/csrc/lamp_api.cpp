@@ -1,0 +1,249 @@
+// C ABI of the mixed-precision tiled attention library: argument validation,
+// instantiation choice, launch on the caller's stream.  No allocation, no
+// synchronisation; the only state is a thread-local error string.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/lamp.h"
+#include "lamp_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+lamp_status fail(lamp_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+lamp_status ok() {
+  g_err[0] = '\0';
+  return LAMP_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+bool is16(int32_t t) { return t == LAMP_F16 || t == LAMP_BF16; }
+bool is8(int32_t t) { return t == LAMP_I8 || t == LAMP_E4M3; }
+bool supported_d(int64_t d) { return d == 64 || d == 128 || d == 256; }
+
+constexpr int64_t kMaxSeq = 1 << 20;   // keeps every in-kernel row index in int32
+constexpr int64_t kMaxGrid = (1ll << 31) - 1;
+
+lamp_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(LAMP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lamp_status_string(lamp_status s) {
+  switch (s) {
+    case LAMP_OK: return "LAMP_OK";
+    case LAMP_ERR_NULL: return "LAMP_ERR_NULL";
+    case LAMP_ERR_SHAPE: return "LAMP_ERR_SHAPE";
+    case LAMP_ERR_UNSUPPORTED: return "LAMP_ERR_UNSUPPORTED";
+    case LAMP_ERR_ALIGN: return "LAMP_ERR_ALIGN";
+    case LAMP_ERR_HIP: return "LAMP_ERR_HIP";
+  }
+  return "LAMP_ERR_UNKNOWN";
+}
+
+const char* lamp_last_error(void) { return g_err; }
+
+int32_t lamp_abi_version(void) { return LAMP_ABI_VERSION; }
+
+lamp_status lamp_quantize_blocks(const void* x, int32_t x_dtype, int64_t B, int64_t H, int64_t S,
+                                 int64_t D, int64_t sb, int64_t sh, int64_t ss,
+                                 int32_t block_rows, int32_t code_dtype, void* codes,
+                                 float* scales, void* stream) {
+  if (B < 0 || H < 0 || S < 0 || D < 0) return fail(LAMP_ERR_SHAPE, "negative size");
+  if (sb < 0 || sh < 0 || ss < 0) return fail(LAMP_ERR_SHAPE, "negative stride");
+  if (!is16(x_dtype)) return fail(LAMP_ERR_UNSUPPORTED, "x_dtype must be LAMP_F16 or LAMP_BF16");
+  if (!is8(code_dtype)) return fail(LAMP_ERR_UNSUPPORTED, "code_dtype must be LAMP_I8 or LAMP_E4M3");
+  if (!supported_d(D)) return fail(LAMP_ERR_UNSUPPORTED, "D=%lld not in {64,128,256}", (long long)D);
+  if (block_rows < 1 || block_rows > 256)
+    return fail(LAMP_ERR_UNSUPPORTED, "block_rows=%d not in [1, 256]", block_rows);
+  if (S > kMaxSeq) return fail(LAMP_ERR_UNSUPPORTED, "S=%lld above %lld", (long long)S, (long long)kMaxSeq);
+  if (B == 0 || H == 0 || S == 0) return ok();
+  if (!x || !codes || !scales) return fail(LAMP_ERR_NULL, "x, codes and scales are required");
+  if (ss < D) return fail(LAMP_ERR_SHAPE, "row stride %lld < D", (long long)ss);
+  if (!aligned16(x) || !aligned16(codes) || (ss % 8) || (sh % 8) || (sb % 8))
+    return fail(LAMP_ERR_ALIGN, "x, codes need 16-byte alignment and strides a multiple of 8");
+  const int64_t nb = cdiv(S, block_rows);
+  if (B * H * nb > kMaxGrid) return fail(LAMP_ERR_UNSUPPORTED, "too many blocks");
+  lamp::QuantArgs a{};
+  a.x = x;
+  a.codes = codes;
+  a.scales = scales;
+  a.sb = sb;
+  a.sh = sh;
+  a.ss = ss;
+  a.B = (int32_t)B;
+  a.H = (int32_t)H;
+  a.S = (int32_t)S;
+  a.D = (int32_t)D;
+  a.block_rows = block_rows;
+  a.nb = (int32_t)nb;
+  a.bf16 = x_dtype == LAMP_BF16;
+  a.e4m3 = code_dtype == LAMP_E4M3;
+  return hip_status(lamp::launch_quantize(a, static_cast<hipStream_t>(stream)), "quantize launch");
+}
+
+lamp_status lamp_build_mask(int64_t B, int64_t Hq, int64_t S_q, int64_t S_k, int32_t tile_m,
+                            int32_t tile_n, int32_t tiles_per_bit, double frac_16bit,
+                            uint64_t seed, uint64_t* mask, int32_t words_per_row,
+                            void* stream) {
+  if (B < 0 || Hq < 0 || S_q < 0 || S_k < 0) return fail(LAMP_ERR_SHAPE, "negative size");
+  if (tile_m <= 0 || tile_n <= 0 || tiles_per_bit <= 0)
+    return fail(LAMP_ERR_SHAPE, "tile sizes and tiles_per_bit must be positive");
+  if (!(frac_16bit >= 0.0 && frac_16bit <= 1.0))
+    return fail(LAMP_ERR_SHAPE, "frac_16bit must lie in [0, 1]");
+  if (S_q > kMaxSeq || S_k > kMaxSeq) return fail(LAMP_ERR_UNSUPPORTED, "sequence too long");
+  const int64_t n_qt = cdiv(S_q, tile_m), n_kt = cdiv(S_k, tile_n);
+  const int64_t n_g = cdiv(n_kt, tiles_per_bit);
+  if (words_per_row < cdiv(n_g, 64) || words_per_row < 1)
+    return fail(LAMP_ERR_UNSUPPORTED, "words_per_row=%d < ceil(n_g/64)=%lld", words_per_row,
+                (long long)cdiv(n_g, 64));
+  if (B == 0 || Hq == 0 || S_q == 0) return ok();
+  if (!mask) return fail(LAMP_ERR_NULL, "mask is required");
+  if (reinterpret_cast<uintptr_t>(mask) & 7u) return fail(LAMP_ERR_ALIGN, "mask needs 8-byte alignment");
+  lamp::MaskArgs a{};
+  a.mask = mask;
+  a.total_words = B * Hq * n_qt * words_per_row;
+  if (cdiv(a.total_words, 256) > kMaxGrid) return fail(LAMP_ERR_UNSUPPORTED, "mask too large");
+  a.seed = seed;
+  // floor(f * 2^32) in double, exact for every double f in [0, 1]
+  a.threshold = (uint64_t)std::floor(frac_16bit * 4294967296.0);
+  a.words_per_row = words_per_row;
+  a.n_g = (int32_t)n_g;
+  return hip_status(lamp::launch_build_mask(a, static_cast<hipStream_t>(stream)), "mask launch");
+}
+
+lamp_status lamp_attn_fwd(const lamp_attn_params* p, void* stream) {
+  if (!p) return fail(LAMP_ERR_NULL, "params is NULL");
+  if (p->struct_size != sizeof(lamp_attn_params))
+    return fail(LAMP_ERR_UNSUPPORTED, "struct_size %u != %zu (ABI mismatch)", p->struct_size,
+                sizeof(lamp_attn_params));
+  if (p->B < 0 || p->Hq < 0 || p->Hkv < 0 || p->S_q < 0 || p->S_k < 0 || p->D < 0)
+    return fail(LAMP_ERR_SHAPE, "negative size");
+  for (int i = 0; i < 3; ++i) {
+    if (p->q_str[i] < 0 || p->k_str[i] < 0 || p->v_str[i] < 0 || p->o_str[i] < 0)
+      return fail(LAMP_ERR_SHAPE, "negative stride");
+  }
+  if (p->mode != LAMP_MODE_MASK && p->mode != LAMP_MODE_ADAPTIVE)
+    return fail(LAMP_ERR_UNSUPPORTED, "mode %d", p->mode);
+  if (!is16(p->in_dtype)) return fail(LAMP_ERR_UNSUPPORTED, "in_dtype must be LAMP_F16 or LAMP_BF16");
+  if (!is8(p->code_dtype)) return fail(LAMP_ERR_UNSUPPORTED, "code_dtype must be LAMP_I8 or LAMP_E4M3");
+  if (!supported_d(p->D)) return fail(LAMP_ERR_UNSUPPORTED, "D=%lld not in {64,128,256}", (long long)p->D);
+  if (p->tile_m != 64 && p->tile_m != 128) return fail(LAMP_ERR_UNSUPPORTED, "tile_m must be 64 or 128");
+  if (p->tile_n != 64) return fail(LAMP_ERR_UNSUPPORTED, "tile_n must be 64");
+  if (p->tiles_per_bit < 1) return fail(LAMP_ERR_SHAPE, "tiles_per_bit must be >= 1");
+  if (p->Hkv == 0 || p->Hq % p->Hkv != 0)
+    return fail(LAMP_ERR_UNSUPPORTED, "Hq=%lld must be a positive multiple of Hkv=%lld",
+                (long long)p->Hq, (long long)p->Hkv);
+  if (p->causal != 0 && p->causal != 1) return fail(LAMP_ERR_SHAPE, "causal must be 0 or 1");
+  if (p->causal && p->S_q != p->S_k) return fail(LAMP_ERR_UNSUPPORTED, "causal needs S_q == S_k");
+  if (p->exp8 != 0 && p->exp8 != 1) return fail(LAMP_ERR_SHAPE, "exp8 must be 0 or 1");
+  if (p->mode == LAMP_MODE_ADAPTIVE) {
+    if (p->sub_rows != 32) return fail(LAMP_ERR_UNSUPPORTED, "sub_rows must be 32");
+    if (std::isnan(p->tau)) return fail(LAMP_ERR_SHAPE, "tau is NaN");
+  }
+  if (std::isnan(p->sm_scale)) return fail(LAMP_ERR_SHAPE, "sm_scale is NaN");
+  if (p->S_q > kMaxSeq || p->S_k > kMaxSeq) return fail(LAMP_ERR_UNSUPPORTED, "sequence too long");
+  const int64_t n_qt = cdiv(p->S_q, p->tile_m), n_kt = cdiv(p->S_k, p->tile_n);
+  const int64_t n_g = cdiv(n_kt, p->tiles_per_bit);
+  if (p->words_per_row < cdiv(n_g, 64) || p->words_per_row < 1)
+    return fail(LAMP_ERR_UNSUPPORTED, "words_per_row=%d < ceil(n_g/64)=%lld", p->words_per_row,
+                (long long)cdiv(n_g, 64));
+  if (p->dbg_qk_acc && p->code_dtype != LAMP_I8)
+    return fail(LAMP_ERR_UNSUPPORTED, "dbg_qk_acc exists on the int8 path only");
+  if (p->B == 0 || p->Hq == 0 || p->S_q == 0) return ok();
+  if (p->S_k == 0) return fail(LAMP_ERR_SHAPE, "S_k == 0 with S_q > 0: softmax over no keys");
+  if (!p->q || !p->k || !p->v || !p->q8 || !p->k8 || !p->q_scale || !p->k_scale || !p->mask ||
+      !p->out)
+    return fail(LAMP_ERR_NULL, "q, k, v, q8, k8, q_scale, k_scale, mask and out are required");
+  const int64_t D = p->D;
+  if (p->q_str[2] < D || p->k_str[2] < D || p->v_str[2] < D || p->o_str[2] < D)
+    return fail(LAMP_ERR_SHAPE, "row stride < D");
+  if (!aligned16(p->q) || !aligned16(p->k) || !aligned16(p->v) || !aligned16(p->out) ||
+      !aligned16(p->q8) || !aligned16(p->k8))
+    return fail(LAMP_ERR_ALIGN, "q, k, v, out, q8, k8 need 16-byte alignment");
+  for (int i = 0; i < 3; ++i) {
+    if ((p->q_str[i] | p->k_str[i] | p->v_str[i] | p->o_str[i]) % 8)
+      return fail(LAMP_ERR_ALIGN, "strides must be multiples of 8 elements");
+  }
+  if (reinterpret_cast<uintptr_t>(p->mask) & 7u) return fail(LAMP_ERR_ALIGN, "mask alignment");
+  if (p->flags_out && (reinterpret_cast<uintptr_t>(p->flags_out) & 7u))
+    return fail(LAMP_ERR_ALIGN, "flags_out alignment");
+  if (p->B * p->Hq * n_qt > kMaxGrid) return fail(LAMP_ERR_UNSUPPORTED, "grid too large");
+
+  lamp::AttnArgs a{};
+  a.q = p->q;
+  a.k = p->k;
+  a.v = p->v;
+  a.q8 = static_cast<const uint8_t*>(p->q8);
+  a.k8 = static_cast<const uint8_t*>(p->k8);
+  a.q_scale = p->q_scale;
+  a.k_scale = p->k_scale;
+  a.mask = p->mask;
+  a.out = p->out;
+  a.lse = p->lse;
+  a.flags = p->mode == LAMP_MODE_ADAPTIVE ? p->flags_out : nullptr;
+  a.dbg = p->dbg_qk_acc;
+  a.q_sb = p->q_str[0];
+  a.q_sh = p->q_str[1];
+  a.q_ss = p->q_str[2];
+  a.k_sb = p->k_str[0];
+  a.k_sh = p->k_str[1];
+  a.k_ss = p->k_str[2];
+  a.v_sb = p->v_str[0];
+  a.v_sh = p->v_str[1];
+  a.v_ss = p->v_str[2];
+  a.o_sb = p->o_str[0];
+  a.o_sh = p->o_str[1];
+  a.o_ss = p->o_str[2];
+  a.B = (int32_t)p->B;
+  a.Hq = (int32_t)p->Hq;
+  a.Hkv = (int32_t)p->Hkv;
+  a.S_q = (int32_t)p->S_q;
+  a.S_k = (int32_t)p->S_k;
+  a.n_qt = (int32_t)n_qt;
+  a.n_kt = (int32_t)n_kt;
+  a.tiles_per_bit = p->tiles_per_bit;
+  a.words_per_row = p->words_per_row;
+  a.heads_per_group = (int32_t)(p->Hq / p->Hkv);
+  a.n_sb = (int32_t)cdiv(p->S_q, 32);
+  a.flag_words = (int32_t)cdiv(n_kt, 64);
+  a.causal = p->causal;
+  a.sm_scale = p->sm_scale > 0.f ? p->sm_scale : (float)(1.0 / std::sqrt((double)D));
+  a.tau = p->tau;
+
+  lamp::AttnConfig c{};
+  c.d = (int)D;
+  c.nw = p->tile_m / 32;
+  c.bf16 = p->in_dtype == LAMP_BF16;
+  c.e4m3 = p->code_dtype == LAMP_E4M3;
+  c.adaptive = p->mode == LAMP_MODE_ADAPTIVE;
+  c.exp8 = p->exp8 != 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  switch (c.d) {
+    case 64: e = lamp::launch_attn_d64(a, c, s); break;
+    case 128: e = lamp::launch_attn_d128(a, c, s); break;
+    default: e = lamp::launch_attn_d256(a, c, s); break;
+  }
+  return hip_status(e, "attention launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,108 @@
+// Device helpers shared by the gfx950 kernels: vector types, MFMA wrappers,
+// 8-bit conversions, 16-bit packing.  gfx950 only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lamp {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+// ---------------------------------------------------------------------------
+// MFMA 32x32 wrappers.  Operand layout (all of them): lane l holds row/column
+// (l % 32) and one contiguous run of the reduction index selected by l / 32.
+// The kernels only rely on A and B sharing that mapping.  Output layout:
+// lane l, register i -> column l % 32, row 8*(i/4) + 4*(l/32) + (i%4).
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__device__ __forceinline__ f32x16 mfma16(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ i32x16 mfma_i8(u32x4 a, u32x4 b, i32x16 c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a),
+                                               __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
+}
+
+// OCP e4m3 x e4m3, K = 64, unit block scales (E8M0 127 = 2^0).
+__device__ __forceinline__ f32x16 mfma_e4m3(u32x4 a0, u32x4 a1, u32x4 b0, u32x4 b1, f32x16 c) {
+  i32x8 a = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+  i32x8 b = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// ---------------------------------------------------------------------------
+// conversions
+// ---------------------------------------------------------------------------
+
+// two fp32 -> two OCP e4m3 codes in the low 16 bits (round-to-nearest-even;
+// callers keep |x| <= 448 so no value saturates or overflows).
+__device__ __forceinline__ uint32_t f32x2_to_e4m3(float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+// e4m3 code pair (low 16 bits) -> two fp32 (exact)
+__device__ __forceinline__ f32x2 e4m3x2_to_f32(uint32_t codes) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8((int)codes, false);
+}
+
+template <bool BF16>
+__device__ __forceinline__ uint32_t pack16x2(float a, float b) {
+  if constexpr (BF16) {
+    bf16x2 r = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, r);
+  } else {
+    f16x2 r = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, r);
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float from16(uint32_t bits16) {
+  if constexpr (BF16) {
+    return __builtin_bit_cast(float, bits16 << 16);
+  } else {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+  }
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// memory helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ u32x4 ld_global16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ u32x4 ld_lds16(const char* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void st_lds16(char* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ void st_lds8(char* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
+
+__device__ __forceinline__ float wave_swap32(float x) { return __shfl_xor(x, 32, 64); }
+
+__device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0ull; }
+
+}  // namespace lamp

@@ -1,0 +1,71 @@
+// Internal launch descriptors shared by the C ABI layer and the kernels.
+// Arguments reach the kernels by value; every field has been validated by
+// the ABI layer before a launcher is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lamp {
+
+struct QuantArgs {
+  const void* x;
+  void* codes;
+  float* scales;
+  int64_t sb, sh, ss;          // element strides of x
+  int32_t B, H, S, D;
+  int32_t block_rows, nb;      // nb = ceil(S / block_rows)
+  bool bf16, e4m3;
+};
+
+struct MaskArgs {
+  uint64_t* mask;
+  int64_t total_words;         // B * Hq * n_qt * words_per_row
+  uint64_t seed;
+  uint64_t threshold;          // floor(frac_16bit * 2^32)
+  int32_t words_per_row;
+  int32_t n_g;
+};
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const uint8_t* q8;
+  const uint8_t* k8;
+  const float* q_scale;
+  const float* k_scale;
+  const uint64_t* mask;
+  void* out;
+  float* lse;
+  uint64_t* flags;
+  int32_t* dbg;
+  int64_t q_sb, q_sh, q_ss;
+  int64_t k_sb, k_sh, k_ss;
+  int64_t v_sb, v_sh, v_ss;
+  int64_t o_sb, o_sh, o_ss;
+  int32_t B, Hq, Hkv, S_q, S_k;
+  int32_t n_qt, n_kt, tiles_per_bit, words_per_row;
+  int32_t heads_per_group;     // Hq / Hkv
+  int32_t n_sb, flag_words;    // ceil(S_q/32), ceil(n_kt/64)
+  int32_t causal;
+  float sm_scale;              // natural-log units
+  float tau;
+};
+
+struct AttnConfig {
+  int d;            // 64 | 128 | 256
+  int nw;           // waves per workgroup = tile_m / 32
+  bool bf16;
+  bool e4m3;
+  bool adaptive;
+  bool exp8;
+};
+
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
+hipError_t launch_build_mask(const MaskArgs& a, hipStream_t s);
+hipError_t launch_attn_d64(const AttnArgs& a, const AttnConfig& c, hipStream_t s);
+hipError_t launch_attn_d128(const AttnArgs& a, const AttnConfig& c, hipStream_t s);
+hipError_t launch_attn_d256(const AttnArgs& a, const AttnConfig& c, hipStream_t s);
+
+}  // namespace lamp

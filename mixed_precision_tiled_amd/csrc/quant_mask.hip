@@ -1,0 +1,155 @@
+// Per-block Q/K quantiser and random packed-mask builder (gfx950).
+//
+// Quantiser: TileMix page, section 2 "The Dual-Path Engine" (Q and K
+// quantised with per-block scale factors); LampAttention abstract (8-bit
+// floating point).  One workgroup per (b, h, block) of block_rows x D
+// elements; HBM-bound: the block is read once into registers, reduced to its
+// absmax, and written back as one byte per element.
+//
+// Mask builder: TileMix page, section 2 "Packed Bitmasks" (per query row,
+// one bit per group of key tiles, 1 = 8-bit).  One thread per uint64 word;
+// each bit is a SplitMix64 draw (Steele, Lea & Flood, OOPSLA 2014) compared
+// with the 16-bit fraction.
+#include "lamp_device.h"
+#include "lamp_internal.h"
+
+namespace lamp {
+
+namespace {
+
+constexpr int kQuantThreads = 256;
+
+template <bool BF16, bool E4M3, int CPT>
+__global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantArgs a) {
+  const int blk = blockIdx.x % a.nb;
+  const int bh = blockIdx.x / a.nb;
+  const int h = bh % a.H;
+  const int b = bh / a.H;
+  const int r0 = blk * a.block_rows;
+  const int rows = min(a.block_rows, a.S - r0);
+  const int cpr = a.D / 8;                      // 8-element chunks per row
+  const int nch = rows * cpr;
+  const char* base = reinterpret_cast<const char*>(a.x) +
+                     2 * (b * a.sb + h * a.sh + (int64_t)r0 * a.ss);
+  const int tid = threadIdx.x;
+
+  u32x4 cache[CPT];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = tid + i * kQuantThreads;
+    if (c < nch) {
+      const int r = c / cpr, col = (c % cpr) * 8;
+      cache[i] = ld_global16(base + 2 * ((int64_t)r * a.ss + col));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        amax = fmaxf(amax, fabsf(from16<BF16>(cache[i][e] & 0xFFFFu)));
+        amax = fmaxf(amax, fabsf(from16<BF16>(cache[i][e] >> 16)));
+      }
+    }
+  }
+  // block absmax: wave butterfly, then across the 4 waves through LDS
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  __shared__ float red[kQuantThreads / 64];
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = red[0];
+#pragma unroll
+  for (int w = 1; w < kQuantThreads / 64; ++w) amax = fmaxf(amax, red[w]);
+
+  const float qmax = E4M3 ? 448.f : 127.f;
+  const bool nz = amax > 0.f;
+  const float scale = nz ? amax / qmax : 0.f;   // IEEE division, RNE
+  const float inv = nz ? qmax / amax : 0.f;
+  if (tid == 0) a.scales[((int64_t)b * a.H + h) * a.nb + blk] = scale;
+
+  uint8_t* out = reinterpret_cast<uint8_t*>(a.codes) + (((int64_t)b * a.H + h) * a.S + r0) * a.D;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = tid + i * kQuantThreads;
+    if (c < nch) {
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        y[2 * e] = from16<BF16>(cache[i][e] & 0xFFFFu) * inv;
+        y[2 * e + 1] = from16<BF16>(cache[i][e] >> 16) * inv;
+      }
+      u32x2 packed;
+      if (!nz) {
+        packed = u32x2{0u, 0u};
+      } else if constexpr (E4M3) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = fminf(fmaxf(y[e], -448.f), 448.f);
+        packed.x = f32x2_to_e4m3(y[0], y[1]) | (f32x2_to_e4m3(y[2], y[3]) << 16);
+        packed.y = f32x2_to_e4m3(y[4], y[5]) | (f32x2_to_e4m3(y[6], y[7]) << 16);
+      } else {
+        uint32_t w[2] = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float r = fminf(fmaxf(__builtin_rintf(y[e]), -127.f), 127.f);
+          w[e >> 2] |= ((uint32_t)(int)r & 0xFFu) << (8 * (e & 3));
+        }
+        packed = u32x2{w[0], w[1]};
+      }
+      const int r = c / cpr, col = (c % cpr) * 8;
+      *reinterpret_cast<u32x2*>(out + (int64_t)r * a.D + col) = packed;
+    }
+  }
+}
+
+template <bool BF16, bool E4M3>
+hipError_t launch_quant_t(const QuantArgs& a, int cpt, hipStream_t s) {
+  dim3 grid((unsigned)((int64_t)a.B * a.H * a.nb)), block(kQuantThreads);
+  switch (cpt) {
+    case 4: hipLaunchKernelGGL((quantize_kernel<BF16, E4M3, 4>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((quantize_kernel<BF16, E4M3, 8>), grid, block, 0, s, a); break;
+    case 16: hipLaunchKernelGGL((quantize_kernel<BF16, E4M3, 16>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((quantize_kernel<BF16, E4M3, 32>), grid, block, 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
+__device__ __forceinline__ uint64_t splitmix64(uint64_t seed, uint64_t n) {
+  uint64_t z = seed + (n + 1ull) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+__global__ __launch_bounds__(256) void build_mask_kernel(MaskArgs a) {
+  const int64_t wid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (wid >= a.total_words) return;
+  const int64_t row = wid / a.words_per_row;        // (b*Hq + h)*n_qt + qt
+  const int w = (int)(wid % a.words_per_row);
+  uint64_t word = 0;
+  const int g0 = w * 64;
+  const int gn = min(64, a.n_g - g0);
+  for (int i = 0; i < gn; ++i) {
+    const uint64_t idx = (uint64_t)row * (uint64_t)a.n_g + (uint64_t)(g0 + i);
+    const uint64_t r = splitmix64(a.seed, idx);
+    const bool is16 = (r >> 32) < a.threshold;
+    word |= (uint64_t)(!is16) << i;
+  }
+  a.mask[wid] = word;
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
+  const int64_t nch = (int64_t)a.block_rows * (a.D / 8);
+  const int need = (int)((nch + kQuantThreads - 1) / kQuantThreads);
+  const int cpt = need <= 4 ? 4 : need <= 8 ? 8 : need <= 16 ? 16 : 32;
+  if (a.bf16) {
+    return a.e4m3 ? launch_quant_t<true, true>(a, cpt, s) : launch_quant_t<true, false>(a, cpt, s);
+  }
+  return a.e4m3 ? launch_quant_t<false, true>(a, cpt, s) : launch_quant_t<false, false>(a, cpt, s);
+}
+
+hipError_t launch_build_mask(const MaskArgs& a, hipStream_t s) {
+  const unsigned blocks = (unsigned)((a.total_words + 255) / 256);
+  hipLaunchKernelGGL(build_mask_kernel, dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace lamp

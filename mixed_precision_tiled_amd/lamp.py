@@ -1,0 +1,213 @@
+"""ctypes binding of liblamp.so (see include/lamp.h).
+
+Argument marshalling only: tensors are turned into device pointers, sizes
+and strides, outputs are allocated with torch when the caller passes none,
+and every call goes to the HIP library on torch's current stream.  There is
+no other implementation behind these functions: if the library is missing
+the import fails.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liblamp.so")
+
+LAMP_OK, LAMP_ERR_NULL, LAMP_ERR_SHAPE, LAMP_ERR_UNSUPPORTED, LAMP_ERR_ALIGN, LAMP_ERR_HIP = range(6)
+LAMP_F16, LAMP_BF16, LAMP_I8, LAMP_E4M3 = range(4)
+LAMP_MODE_MASK, LAMP_MODE_ADAPTIVE = 0, 1
+
+_DT16 = {torch.float16: LAMP_F16, torch.bfloat16: LAMP_BF16}
+_CODE = {"i8": LAMP_I8, "e4m3": LAMP_E4M3, LAMP_I8: LAMP_I8, LAMP_E4M3: LAMP_E4M3}
+
+
+class LampError(RuntimeError):
+    def __init__(self, status, detail):
+        self.status = status
+        super().__init__(f"{_status_name(status)}: {detail}")
+
+
+def library_path():
+    return _LIB_PATH
+
+
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(f"{_LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; "
+                      f"g.build()'` (hipcc, gfx950) first")
+_lib = ctypes.CDLL(_LIB_PATH)
+
+_i64, _i32, _u32, _u64 = ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32, ctypes.c_uint64
+_vp, _fp = ctypes.c_void_p, ctypes.POINTER(ctypes.c_float)
+
+
+class lamp_attn_params(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", _u32), ("mode", _i32), ("causal", _i32), ("sm_scale", ctypes.c_float),
+        ("B", _i64), ("Hq", _i64), ("Hkv", _i64), ("S_q", _i64), ("S_k", _i64), ("D", _i64),
+        ("q", _vp), ("k", _vp), ("v", _vp), ("in_dtype", _i32), ("code_dtype", _i32),
+        ("q_str", _i64 * 3), ("k_str", _i64 * 3), ("v_str", _i64 * 3), ("o_str", _i64 * 3),
+        ("q8", _vp), ("k8", _vp), ("q_scale", _vp), ("k_scale", _vp), ("mask", _vp),
+        ("words_per_row", _i32), ("tile_m", _i32), ("tile_n", _i32), ("tiles_per_bit", _i32),
+        ("exp8", _i32), ("tau", ctypes.c_float), ("sub_rows", _i32),
+        ("out", _vp), ("lse", _vp), ("flags_out", _vp), ("dbg_qk_acc", _vp),
+    ]
+
+
+_lib.lamp_quantize_blocks.restype = _i32
+_lib.lamp_quantize_blocks.argtypes = [_vp, _i32, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i32,
+                                      _i32, _vp, _vp, _vp]
+_lib.lamp_build_mask.restype = _i32
+_lib.lamp_build_mask.argtypes = [_i64, _i64, _i64, _i64, _i32, _i32, _i32, ctypes.c_double, _u64,
+                                 _vp, _i32, _vp]
+_lib.lamp_attn_fwd.restype = _i32
+_lib.lamp_attn_fwd.argtypes = [ctypes.POINTER(lamp_attn_params), _vp]
+_lib.lamp_status_string.restype = ctypes.c_char_p
+_lib.lamp_status_string.argtypes = [_i32]
+_lib.lamp_last_error.restype = ctypes.c_char_p
+_lib.lamp_last_error.argtypes = []
+_lib.lamp_abi_version.restype = _i32
+_lib.lamp_abi_version.argtypes = []
+
+
+def _status_name(s):
+    return _lib.lamp_status_string(s).decode()
+
+
+def lamp_status_string(s):
+    return _status_name(s)
+
+
+def lamp_last_error():
+    return _lib.lamp_last_error().decode()
+
+
+def lamp_abi_version():
+    return int(_lib.lamp_abi_version())
+
+
+def exported_symbols(names):
+    """The subset of ``names`` that the loaded library exports."""
+    out = []
+    for n in names:
+        try:
+            getattr(_lib, n)
+            out.append(n)
+        except AttributeError:
+            pass
+    return out
+
+
+def _check(status):
+    if status != LAMP_OK:
+        raise LampError(status, lamp_last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _strides3(t):
+    if t.stride(3) != 1:
+        raise ValueError("the head dimension must be contiguous")
+    return (_i64 * 3)(t.stride(0), t.stride(1), t.stride(2))
+
+
+def cdiv(a, b):
+    return -(-a // b)
+
+
+def lamp_quantize_blocks(x, block_rows, code, codes=None, scales=None):
+    """Per-block quantisation of x [B, H, S, D] (fp16/bf16 CUDA tensor).
+
+    Returns (codes uint8 [B, H, S, D], scales float32 [B, H, ceil(S/block_rows)]).
+    """
+    B, H, S, D = x.shape
+    nb = cdiv(S, block_rows)
+    if codes is None:
+        codes = torch.empty((B, H, S, D), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((B, H, nb), dtype=torch.float32, device=x.device)
+    if x.dtype not in _DT16:
+        raise TypeError("x must be float16 or bfloat16")
+    if x.stride(3) != 1 or not codes.is_contiguous() or not scales.is_contiguous():
+        raise ValueError("x needs a contiguous head dim; codes and scales must be contiguous")
+    _check(_lib.lamp_quantize_blocks(_ptr(x), _DT16[x.dtype], B, H, S, D, x.stride(0), x.stride(1),
+                                     x.stride(2), block_rows, _CODE[code], _ptr(codes),
+                                     _ptr(scales), _stream(x)))
+    return codes, scales
+
+
+def lamp_build_mask(B, Hq, S_q, S_k, tile_m, tile_n, tiles_per_bit, frac_16bit, seed,
+                    words_per_row=None, mask=None, device="cuda"):
+    """Random packed mask, int64 tensor [B, Hq, n_qt, W] holding the uint64 words."""
+    n_qt = cdiv(S_q, tile_m)
+    n_g = cdiv(cdiv(S_k, tile_n), tiles_per_bit)
+    W = words_per_row or max(1, cdiv(n_g, 64))
+    if mask is None:
+        mask = torch.empty((B, Hq, n_qt, W), dtype=torch.int64, device=device)
+    if not mask.is_contiguous():
+        raise ValueError("mask must be contiguous")
+    _check(_lib.lamp_build_mask(B, Hq, S_q, S_k, tile_m, tile_n, tiles_per_bit, float(frac_16bit),
+                                seed & ((1 << 64) - 1), _ptr(mask), W, _stream(mask)))
+    return mask
+
+
+def lamp_attn_fwd(q, k, v, q8, k8, q_scale, k_scale, mask, *, code, causal, tile_m,
+                  tiles_per_bit, tile_n=64, words_per_row=None, mode=LAMP_MODE_MASK, exp8=False,
+                  tau=4.0, sub_rows=32, sm_scale=0.0, out=None, lse=None, flags_out=None,
+                  dbg_qk_acc=None):
+    """Dual-path attention forward.  q [B,Hq,S_q,D], k/v [B,Hkv,S_k,D] 16-bit,
+    q8/k8 codes and q_scale/k_scale from lamp_quantize_blocks, mask from
+    lamp_build_mask.  Returns out [B,Hq,S_q,D] (q's dtype)."""
+    B, Hq, S_q, D = q.shape
+    _, Hkv, S_k, _ = k.shape
+    if q.dtype not in _DT16 or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share float16 or bfloat16")
+    if out is None:
+        out = torch.empty((B, Hq, S_q, D), dtype=q.dtype, device=q.device)
+    W = words_per_row or mask.shape[-1]
+    for t in (q8, k8, q_scale, k_scale, mask, lse, flags_out, dbg_qk_acc):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("codes, scales, mask and optional outputs must be contiguous")
+    p = lamp_attn_params()
+    p.struct_size = ctypes.sizeof(lamp_attn_params)
+    p.mode = mode
+    p.causal = int(bool(causal))
+    p.sm_scale = sm_scale
+    p.B, p.Hq, p.Hkv, p.S_q, p.S_k, p.D = B, Hq, Hkv, S_q, S_k, D
+    p.q, p.k, p.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
+    p.in_dtype = _DT16[q.dtype]
+    p.code_dtype = _CODE[code]
+    p.q_str, p.k_str, p.v_str, p.o_str = _strides3(q), _strides3(k), _strides3(v), _strides3(out)
+    p.q8, p.k8 = q8.data_ptr(), k8.data_ptr()
+    p.q_scale, p.k_scale = q_scale.data_ptr(), k_scale.data_ptr()
+    p.mask = mask.data_ptr()
+    p.words_per_row = W
+    p.tile_m, p.tile_n, p.tiles_per_bit = tile_m, tile_n, tiles_per_bit
+    p.exp8 = int(bool(exp8))
+    p.tau = tau
+    p.sub_rows = sub_rows
+    p.out = out.data_ptr()
+    p.lse = None if lse is None else lse.data_ptr()
+    p.flags_out = None if flags_out is None else flags_out.data_ptr()
+    p.dbg_qk_acc = None if dbg_qk_acc is None else dbg_qk_acc.data_ptr()
+    _check(_lib.lamp_attn_fwd(ctypes.byref(p), _stream(q)))
+    return out
+
+
+def flags_shape(B, Hq, S_q, S_k, tile_n=64, sub_rows=32):
+    return (B, Hq, cdiv(S_q, sub_rows), max(1, cdiv(cdiv(S_k, tile_n), 64)))
+
+
+def fa_flops(B, Hq, S, D, causal):
+    f = 4.0 * B * Hq * S * S * D
+    return f / 2 if causal else f
+
+
+__all__ = [n for n in dir() if n.startswith("lamp_") or n.startswith("LAMP_")] + [
+    "LampError", "library_path", "exported_symbols", "flags_shape", "fa_flops"]

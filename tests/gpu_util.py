@@ -1,0 +1,80 @@
+"""Helpers for the GPU parity tests: run the HIP pipeline through the C ABI
+binding and build the oracle's view of the same seeded inputs."""
+import numpy as np
+import torch
+
+from oracle import attention as A
+from oracle import mask as omask
+
+
+def device():
+    return torch.device("cuda:0")
+
+
+def u64(t):
+    return t.cpu().numpy().view(np.uint64)
+
+
+def gpu_run(cfg, q, k, v, *, lse=True, flags=None, dbg=False, mask_words=None):
+    """Quantise, build the mask (unless given) and run attention on the GPU."""
+    import mixed_precision_tiled_amd as L
+    dev = device()
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    S_q, S_k = q.shape[2], k.shape[2]
+    q8, sq = L.lamp_quantize_blocks(qd, cfg.tile_m, cfg.code)
+    k8, sk = L.lamp_quantize_blocks(kd, cfg.tile_n, cfg.code)
+    n_g = -(-(-(-S_k // cfg.tile_n)) // cfg.tiles_per_bit)
+    W = max(1, -(-n_g // 64))
+    if mask_words is not None:
+        mask = torch.from_numpy(np.ascontiguousarray(mask_words).view(np.int64)).to(dev)
+    elif cfg.mask_all_ones:
+        mask = L.lamp_build_mask(cfg.B, cfg.Hq, S_q, S_k, cfg.tile_m, cfg.tile_n,
+                                 cfg.tiles_per_bit, 0.0, cfg.mask_seed, W, device=dev)
+    else:
+        mask = L.lamp_build_mask(cfg.B, cfg.Hq, S_q, S_k, cfg.tile_m, cfg.tile_n,
+                                 cfg.tiles_per_bit, cfg.frac_16bit, cfg.mask_seed, W, device=dev)
+    lse_t = torch.full((cfg.B, cfg.Hq, S_q), float("nan"), device=dev) if lse else None
+    flags_t = None
+    if cfg.adaptive and flags is not False:
+        flags_t = torch.full(L.lamp.flags_shape(cfg.B, cfg.Hq, S_q, S_k), -1, dtype=torch.int64,
+                             device=dev)
+    dbg_t = None
+    if dbg:
+        dbg_t = torch.full((cfg.B, cfg.Hq, S_q, S_k), -(2 ** 31), dtype=torch.int32, device=dev)
+    out = L.lamp_attn_fwd(qd, kd, vd, q8, k8, sq, sk, mask, code=cfg.code, causal=cfg.causal,
+                          tile_m=cfg.tile_m, tiles_per_bit=cfg.tiles_per_bit,
+                          mode=L.LAMP_MODE_ADAPTIVE if cfg.adaptive else L.LAMP_MODE_MASK,
+                          exp8=cfg.exp8, tau=cfg.tau, sub_rows=cfg.sub_rows,
+                          sm_scale=cfg.sm_scale, lse=lse_t, flags_out=flags_t, dbg_qk_acc=dbg_t)
+    torch.cuda.synchronize()
+    return dict(q8=q8.cpu().numpy(), sq=sq.cpu().numpy(), k8=k8.cpu().numpy(),
+                sk=sk.cpu().numpy(), mask=u64(mask), out=out.float().cpu().numpy(),
+                lse=None if lse_t is None else lse_t.cpu().numpy(),
+                flags=None if flags_t is None else u64(flags_t),
+                dbg=None if dbg_t is None else dbg_t.cpu().numpy())
+
+
+def oracle_mask(cfg, S_q, S_k):
+    n_g = -(-(-(-S_k // cfg.tile_n)) // cfg.tiles_per_bit)
+    W = max(1, -(-n_g // 64))
+    f16 = 0.0 if cfg.mask_all_ones else cfg.frac_16bit
+    return omask.build_mask(cfg.B, cfg.Hq, S_q, S_k, cfg.tile_m, cfg.tile_n, cfg.tiles_per_bit,
+                            f16, cfg.mask_seed, W)
+
+
+def oracle_problem(cfg, q, k, v, b=None, h=None, mask_words=None):
+    """Oracle Problem for all heads, or for the single query head (b, h) and
+    its KV head (quantisation blocks never cross heads, so this is exact)."""
+    S_q, S_k = q.shape[2], k.shape[2]
+    mw = oracle_mask(cfg, S_q, S_k) if mask_words is None else mask_words
+    qn, kn, vn = (t.double().numpy() for t in (q, k, v))
+    if b is not None:
+        kvh = h // (cfg.Hq // cfg.Hkv)
+        qn = qn[b:b + 1, h:h + 1]
+        kn, vn = kn[b:b + 1, kvh:kvh + 1], vn[b:b + 1, kvh:kvh + 1]
+        mw = mw[b:b + 1, h:h + 1]
+    return A.make_problem(qn, kn, vn, causal=cfg.causal, code=cfg.code, tile_m=cfg.tile_m,
+                          tile_n=cfg.tile_n, tiles_per_bit=cfg.tiles_per_bit,
+                          frac_16bit=cfg.frac_16bit, seed=cfg.mask_seed, mask_words=mw,
+                          sm_scale=cfg.sm_scale, adaptive=cfg.adaptive, exp8=cfg.exp8,
+                          tau=cfg.tau, sub_rows=cfg.sub_rows)
