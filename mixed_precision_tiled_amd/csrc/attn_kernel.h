@@ -66,12 +66,23 @@ __device__ __forceinline__ int vt_off(int d, int ch) {
   return d * 128 + ((ch ^ ((d ^ (d >> 3)) & 7)) << 4);
 }
 
-template <int D, int NW, bool BF16, bool E4M3, bool ADAPTIVE, bool EXP8>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
+// Waves per SIMD the register budget is sized for: two for D <= 128 so that
+// one wave's MFMAs overlap the other's softmax arithmetic, one for D = 256.
+template <int D>
+struct AttnOccupancy {
+  static constexpr int kWavesPerEU = D <= 128 ? 2 : 1;
+};
+
+template <int D, int NW, bool BF16, bool E4M3, bool ADAPTIVE, bool EXP8, bool DBG>
+__global__ __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(AttnOccupancy<D>::kWavesPerEU, AttnOccupancy<D>::kWavesPerEU)))
+void attn_fwd_kernel(const AttnArgs a) {
   using SH = AttnShape<D, NW>;
-  // lazy rescale with base-2 logits is exact in exact arithmetic and is used
-  // whenever no 8-bit rounding or flag decision depends on the running max
+  // base-2 logits with a lazily moved reference maximum (exact in exact
+  // arithmetic); used whenever no 8-bit rounding or flag decision depends on
+  // the running maximum
   constexpr bool LAZY = !ADAPTIVE && !EXP8;
+  constexpr float kLogScale = LAZY ? kLog2e : 1.f;
   __shared__ __attribute__((aligned(16))) char smem[2 * SH::STAGE];
 
   // ---- workgroup -> (b, h, qt): XCD-contiguous chunks of the logical order
@@ -99,6 +110,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
   const int w_last = min(a.S_q, row0 + 32) - 1;
   const int kt_end_w = !wave_live ? 0 : (a.causal ? min(a.n_kt, w_last / 64 + 1) : a.n_kt);
   const bool rows_ragged = row0 + 32 > a.S_q;
+  // largest valid key index of this lane's row (-1: row beyond S_q)
+  const int key_lim = my_row >= a.S_q ? -1 : (a.causal ? min(my_row, a.S_k - 1) : a.S_k - 1);
 
   // ---- Q fragments (B operand of S^T = K Q^T), resident for the whole loop
   const char* qp = reinterpret_cast<const char*>(a.q) +
@@ -121,17 +134,27 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
   const float sQ = a.q_scale[((int64_t)b * a.Hq + h) * a.n_qt + qt];
   const uint64_t* mrow = a.mask + (((int64_t)b * a.Hq + h) * a.n_qt + qt) * a.words_per_row;
 
-  const char* kp = reinterpret_cast<const char*>(a.k) + 2 * (b * a.k_sb + kvh * a.k_sh);
-  const char* vp = reinterpret_cast<const char*>(a.v) + 2 * (b * a.v_sb + kvh * a.v_sh);
-  const uint8_t* k8p = a.k8 + ((int64_t)b * a.Hkv + kvh) * a.S_k * D;
+  // per-head bases; offsets inside a head fit 32 bits (validated S <= 2^20)
+  const char* kbase = reinterpret_cast<const char*>(a.k) + 2 * (b * a.k_sb + kvh * a.k_sh);
+  const char* vbase = reinterpret_cast<const char*>(a.v) + 2 * (b * a.v_sb + kvh * a.v_sh);
+  const uint8_t* k8base = a.k8 + ((int64_t)b * a.Hkv + kvh) * a.S_k * D;
   const float* sKp = a.k_scale + ((int64_t)b * a.Hkv + kvh) * a.n_kt;
+  const uint32_t kss = 2u * (uint32_t)a.k_ss, vss = 2u * (uint32_t)a.v_ss;
+  const int key_max = a.S_k - 1;
 
   auto tile_is8 = [&](int kt) -> bool {
     const int g = kt / a.tiles_per_bit;
     return (mrow[g >> 6] >> (g & 63)) & 1ull;
   };
 
-  // ---- global -> register staging of one key tile ----
+  // ---- global -> register staging of one key tile.  Thread mapping:
+  // K16 chunk (row kr16 + i*NT/CH16, chunk kc16), K8 likewise, V block of
+  // 4 keys (4*(vkg + i*NT/(D/8)) ...) x 8 dims (8*vdc ...) ----
+  const int kc16 = tid % SH::CH16, kr16 = tid / SH::CH16;
+  const int kc8 = tid % SH::CH8, kr8 = tid / SH::CH8;
+  const int vdc = tid % (D / 8), vkg = tid / (D / 8);
+  constexpr int R16_STEP = SH::NT / SH::CH16, R8_STEP = SH::NT / SH::CH8;
+  constexpr int VKG_STEP = SH::NT / (D / 8);
   u32x4 kst[SH::LD_K16];
   u32x4 vst[4 * SH::LD_V];
   auto load_tile = [&](int kt, bool is8) {
@@ -139,33 +162,27 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
     if (is8) {
 #pragma unroll
       for (int i = 0; i < SH::LD_K8; ++i) {
-        const int c = tid + i * SH::NT;
-        if (SH::N_K8 % SH::NT == 0 || c < SH::N_K8) {
-          const int r = c / SH::CH8, ch = c % SH::CH8;
-          const int key = min(key0 + r, a.S_k - 1);
-          kst[i] = ld_global16(k8p + (int64_t)key * D + ch * 16);
+        if (SH::N_K8 % SH::NT == 0 || tid + i * SH::NT < SH::N_K8) {
+          const int key = min(key0 + kr8 + i * R8_STEP, key_max);
+          kst[i] = ld_global16(k8base + (uint32_t)(key * D + kc8 * 16));
         }
       }
     } else {
 #pragma unroll
       for (int i = 0; i < SH::LD_K16; ++i) {
-        const int c = tid + i * SH::NT;
-        if (SH::N_K16 % SH::NT == 0 || c < SH::N_K16) {
-          const int r = c / SH::CH16, ch = c % SH::CH16;
-          const int key = min(key0 + r, a.S_k - 1);
-          kst[i] = ld_global16(kp + 2 * ((int64_t)key * a.k_ss + ch * 8));
+        if (SH::N_K16 % SH::NT == 0 || tid + i * SH::NT < SH::N_K16) {
+          const int key = min(key0 + kr16 + i * R16_STEP, key_max);
+          kst[i] = ld_global16(kbase + ((uint32_t)key * kss + (uint32_t)kc16 * 16u));
         }
       }
     }
 #pragma unroll
     for (int i = 0; i < SH::LD_V; ++i) {
-      const int bi = tid + i * SH::NT;
-      if (SH::N_V % SH::NT == 0 || bi < SH::N_V) {
-        const int dc = bi % (D / 8), kg = bi / (D / 8);
+      if (SH::N_V % SH::NT == 0 || tid + i * SH::NT < SH::N_V) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int key = min(key0 + 4 * kg + r, a.S_k - 1);
-          vst[4 * i + r] = ld_global16(vp + 2 * ((int64_t)key * a.v_ss + dc * 8));
+          const int key = min(key0 + 4 * (vkg + i * VKG_STEP) + r, key_max);
+          vst[4 * i + r] = ld_global16(vbase + ((uint32_t)key * vss + (uint32_t)vdc * 16u));
         }
       }
     }
@@ -176,19 +193,15 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
     if (is8) {
 #pragma unroll
       for (int i = 0; i < SH::LD_K8; ++i) {
-        const int c = tid + i * SH::NT;
-        if (SH::N_K8 % SH::NT == 0 || c < SH::N_K8) {
-          const int r = c / SH::CH8, ch = c % SH::CH8;
-          st_lds16(kb + k_off<SH::M8>(r, ch, D), kst[i]);
+        if (SH::N_K8 % SH::NT == 0 || tid + i * SH::NT < SH::N_K8) {
+          st_lds16(kb + k_off<SH::M8>(kr8 + i * R8_STEP, kc8, D), kst[i]);
         }
       }
     } else {
 #pragma unroll
       for (int i = 0; i < SH::LD_K16; ++i) {
-        const int c = tid + i * SH::NT;
-        if (SH::N_K16 % SH::NT == 0 || c < SH::N_K16) {
-          const int r = c / SH::CH16, ch = c % SH::CH16;
-          st_lds16(kb + k_off<SH::M16>(r, ch, 2 * D), kst[i]);
+        if (SH::N_K16 % SH::NT == 0 || tid + i * SH::NT < SH::N_K16) {
+          st_lds16(kb + k_off<SH::M16>(kr16 + i * R16_STEP, kc16, 2 * D), kst[i]);
         }
       }
     }
@@ -197,14 +210,13 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
     // one 16-byte LDS chunk holds keys {4h..4h+3, 8+4h..8+4h+3} for h = 0, 1
 #pragma unroll
     for (int i = 0; i < SH::LD_V; ++i) {
-      const int bi = tid + i * SH::NT;
-      if (SH::N_V % SH::NT == 0 || bi < SH::N_V) {
-        const int dc = bi % (D / 8), kg = bi / (D / 8);
+      if (SH::N_V % SH::NT == 0 || tid + i * SH::NT < SH::N_V) {
+        const int kg = vkg + i * VKG_STEP;
         const int g16 = kg >> 2, qq = kg & 3;
         const int ch = 2 * g16 + (qq & 1), half = qq >> 1;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int d = 8 * dc + e;
+          const int d = 8 * vdc + e;
           const int we = e >> 1;
           uint32_t lo, hi;
           if (e & 1) {
@@ -233,6 +245,77 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
   uint64_t* frow = (ADAPTIVE && a.flags != nullptr && wave_live)
                        ? a.flags + (((int64_t)b * a.Hq + h) * a.n_sb + sb_index) * a.flag_words
                        : nullptr;
+  const float sm = a.sm_scale;
+
+  // element e of x[] (key block e/16, accumulator register e%16) holds key
+  // key0 + kofs(e) + 4*hf of query row my_row
+  auto kofs = [](int e) { return (e >> 4) * 32 + ((e & 15) >> 2) * 8 + (e & 3); };
+
+  auto qk16_lds = [&](const char* kb, float* x) {
+#pragma unroll
+    for (int kb_ = 0; kb_ < 2; ++kb_) {
+      f32x16 acc = f32x16{};
+      const int r = kb_ * 32 + lr;
+#pragma unroll
+      for (int t = 0; t < SH::NQ16; ++t) {
+        const u32x4 af = ld_lds16(kb + k_off<SH::M16>(r, 2 * t + hf, 2 * D));
+        acc = mfma16<BF16>(af, q16[t], acc);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[kb_ * 16 + i] = acc[i];
+    }
+  };
+  auto qk16_global = [&](int key0, float* x) {
+#pragma unroll
+    for (int kb_ = 0; kb_ < 2; ++kb_) {
+      f32x16 acc = f32x16{};
+      const int key = min(key0 + kb_ * 32 + lr, key_max);
+      const char* kr = kbase + (uint32_t)key * kss;
+#pragma unroll
+      for (int t = 0; t < SH::NQ16; ++t) {
+        const u32x4 af = ld_global16(kr + 2 * (16 * t + 8 * hf));
+        acc = mfma16<BF16>(af, q16[t], acc);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[kb_ * 16 + i] = acc[i];
+    }
+  };
+  auto qk8_lds = [&](const char* kb, int key0, float* x) {
+#pragma unroll
+    for (int kb_ = 0; kb_ < 2; ++kb_) {
+      const int r = kb_ * 32 + lr;
+      if constexpr (E4M3) {
+        f32x16 acc = f32x16{};
+#pragma unroll
+        for (int t = 0; t < D / 64; ++t) {
+          const u32x4 a0 = ld_lds16(kb + k_off<SH::M8>(r, 4 * t + 2 * hf, D));
+          const u32x4 a1 = ld_lds16(kb + k_off<SH::M8>(r, 4 * t + 2 * hf + 1, D));
+          acc = mfma_e4m3(a0, a1, q8[2 * t], q8[2 * t + 1], acc);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[kb_ * 16 + i] = acc[i];
+      } else {
+        i32x16 acc = i32x16{};
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t) {
+          const u32x4 af = ld_lds16(kb + k_off<SH::M8>(r, 2 * t + hf, D));
+          acc = mfma_i8(af, q8[t], acc);
+        }
+        if constexpr (DBG) {
+          if (my_row < a.S_q) {
+            int32_t* dr = a.dbg + (((int64_t)b * a.Hq + h) * a.S_q + my_row) * a.S_k;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int j = key0 + kofs(kb_ * 16 + i) + 4 * hf;
+              if (j < a.S_k) dr[j] = acc[i];
+            }
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[kb_ * 16 + i] = (float)acc[i];
+      }
+    }
+  };
 
   auto compute_tile = [&](int kt, int buf, bool is8) {
     const char* kb = smem + buf * SH::STAGE;
@@ -240,78 +323,35 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
     const int key0 = kt * SH::TN;
     const bool need_mask = rows_ragged || (key0 + SH::TN > a.S_k) ||
                            (a.causal && key0 + SH::TN - 1 > row0);
-    float s[32];
+    // valid(e) <=> kofs(e) <= lim_rel
+    const int lim_rel = key_lim - key0 - 4 * hf;
+    float x[32];
+    float c;                 // logit = x * c (base-2 units when LAZY)
     bool is16 = !is8;
+    bool scaled = false;     // x already holds c * x with invalid entries -inf
 
-    auto apply_mask = [&]() {
-      if (need_mask) {
+    auto mask_scale = [&]() {
 #pragma unroll
-        for (int e = 0; e < 32; ++e) {
-          const int kb_ = e >> 4, i = e & 15;
-          const int j = key0 + kb_ * 32 + (i >> 2) * 8 + hf * 4 + (i & 3);
-          const bool ok = j < a.S_k && my_row < a.S_q && (!a.causal || j <= my_row);
-          s[e] = ok ? s[e] : kNegInf;
-        }
-      }
-    };
-    auto qk16_from_lds = [&](float scale) {
-#pragma unroll
-      for (int kb_ = 0; kb_ < 2; ++kb_) {
-        f32x16 acc = f32x16{};
-        const int r = kb_ * 32 + lr;
-#pragma unroll
-        for (int t = 0; t < SH::NQ16; ++t) {
-          const u32x4 af = ld_lds16(kb + k_off<SH::M16>(r, 2 * t + hf, 2 * D));
-          acc = mfma16<BF16>(af, q16[t], acc);
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[kb_ * 16 + i] = acc[i] * scale;
-      }
+      for (int e = 0; e < 32; ++e) x[e] = kofs(e) <= lim_rel ? x[e] * c : kNegInf;
+      scaled = true;
     };
 
-    const float sm = a.sm_scale;
     if (is8) {
-      const float c8 = (sQ * sKp[kt]) * sm;
-      const float sc = LAZY ? c8 * kLog2e : c8;
-#pragma unroll
-      for (int kb_ = 0; kb_ < 2; ++kb_) {
-        const int r = kb_ * 32 + lr;
-        if constexpr (E4M3) {
-          f32x16 acc = f32x16{};
-#pragma unroll
-          for (int t = 0; t < D / 64; ++t) {
-            const u32x4 a0 = ld_lds16(kb + k_off<SH::M8>(r, 4 * t + 2 * hf, D));
-            const u32x4 a1 = ld_lds16(kb + k_off<SH::M8>(r, 4 * t + 2 * hf + 1, D));
-            acc = mfma_e4m3(a0, a1, q8[2 * t], q8[2 * t + 1], acc);
-          }
-#pragma unroll
-          for (int i = 0; i < 16; ++i) s[kb_ * 16 + i] = acc[i] * sc;
-        } else {
-          i32x16 acc = i32x16{};
-#pragma unroll
-          for (int t = 0; t < D / 32; ++t) {
-            const u32x4 af = ld_lds16(kb + k_off<SH::M8>(r, 2 * t + hf, D));
-            acc = mfma_i8(af, q8[t], acc);
-          }
-          if (a.dbg != nullptr && my_row < a.S_q) {
-            int32_t* dr = a.dbg + (((int64_t)b * a.Hq + h) * a.S_q + my_row) * a.S_k;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int j = key0 + kb_ * 32 + (i >> 2) * 8 + hf * 4 + (i & 3);
-              if (j < a.S_k) dr[j] = acc[i];
-            }
-          }
-#pragma unroll
-          for (int i = 0; i < 16; ++i) s[kb_ * 16 + i] = (float)acc[i] * sc;
-        }
-      }
-      apply_mask();
-      if constexpr (ADAPTIVE) {
+      qk8_lds(kb, key0, x);
+      c = (sQ * sKp[kt]) * sm * kLogScale;
+    } else {
+      qk16_lds(kb, x);
+      c = sm * kLogScale;
+    }
+    if (need_mask) mask_scale();
+    if constexpr (ADAPTIVE) {
+      if (is8) {
         // look-ahead: m' = max(m, rowmax s8); flag the 32-row sub-block if
         // some valid 8-bit logit is within tau of m'
-        float mx8 = s[0];
+        float mx8 = x[0];
 #pragma unroll
-        for (int e = 1; e < 32; ++e) mx8 = fmaxf(mx8, s[e]);
+        for (int e = 1; e < 32; ++e) mx8 = fmaxf(mx8, x[e]);
+        if (!scaled) mx8 *= c;
         mx8 = fmaxf(mx8, wave_swap32(mx8));
         const float mprime = fmaxf(m_run, mx8);
         const bool cond = (mx8 != kNegInf) && (mx8 - mprime >= -a.tau);
@@ -320,37 +360,24 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
           fword |= 1ull << (kt & 63);
           // recompute the sub-block's logits at 16 bits, K16 straight from
           // global memory (only flagged sub-blocks need it)
-#pragma unroll
-          for (int kb_ = 0; kb_ < 2; ++kb_) {
-            f32x16 acc = f32x16{};
-            const int key = min(key0 + kb_ * 32 + lr, a.S_k - 1);
-            const char* kr = kp + 2 * ((int64_t)key * a.k_ss);
-#pragma unroll
-            for (int t = 0; t < SH::NQ16; ++t) {
-              const u32x4 af = ld_global16(kr + 2 * (16 * t + 8 * hf));
-              acc = mfma16<BF16>(af, q16[t], acc);
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) s[kb_ * 16 + i] = acc[i] * sm;
-          }
-          apply_mask();
+          qk16_global(key0, x);
+          c = sm;
+          scaled = false;
+          if (need_mask) mask_scale();
         }
       }
-    } else {
-      qk16_from_lds(LAZY ? sm * kLog2e : sm);
-      apply_mask();
     }
-
-    // ---- shared online-softmax update ----
-    float mx = s[0];
+    const float cm = scaled ? 1.f : c;
+    float mx = x[0];
 #pragma unroll
-    for (int e = 1; e < 32; ++e) mx = fmaxf(mx, s[e]);
+    for (int e = 1; e < 32; ++e) mx = fmaxf(mx, x[e]);
+    mx *= cm;
     mx = fmaxf(mx, wave_swap32(mx));
-    float p[32];
+
+    // ---- shared online-softmax update; x[] becomes p ----
     if constexpr (LAZY) {
-      // base-2 logits; the reference max only moves when a row's max grows
-      // by more than 8 (p <= 2^8 in between), which changes no result in
-      // exact arithmetic
+      // the reference maximum only moves when a row's max grows by more
+      // than 8 (so p <= 2^8 in between)
       if (wave_any(mx > m_run + 8.f)) {
         const float m_new = fmaxf(m_run, mx);
         const float alpha = (m_new == kNegInf) ? 1.f : exp2_fast(m_run - m_new);
@@ -361,7 +388,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
       }
       const float msub = (m_run == kNegInf) ? 0.f : m_run;
 #pragma unroll
-      for (int e = 0; e < 32; ++e) p[e] = exp2_fast(s[e] - msub);
+      for (int e = 0; e < 32; ++e) x[e] = exp2_fast(__builtin_fmaf(x[e], cm, -msub));
     } else {
       const float m_new = fmaxf(m_run, mx);
       if (wave_any(m_new != m_run)) {
@@ -376,34 +403,35 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
         // x = s - m rounded to e4m3, exp, rounded to e4m3 again
 #pragma unroll
         for (int e = 0; e < 32; e += 2) {
-          const float x0 = fmaxf(s[e] - msub, -448.f);
-          const float x1 = fmaxf(s[e + 1] - msub, -448.f);
+          const float x0 = fmaxf(__builtin_fmaf(x[e], cm, -msub), -448.f);
+          const float x1 = fmaxf(__builtin_fmaf(x[e + 1], cm, -msub), -448.f);
           const f32x2 xq = e4m3x2_to_f32(f32x2_to_e4m3(x0, x1));
           const float e0 = exp2_fast(xq.x * kLog2e);
           const float e1 = exp2_fast(xq.y * kLog2e);
           const f32x2 pq = e4m3x2_to_f32(f32x2_to_e4m3(e0, e1));
-          p[e] = pq.x;
-          p[e + 1] = pq.y;
+          x[e] = pq.x;
+          x[e + 1] = pq.y;
         }
       } else {
+        const float c2 = cm * kLog2e, m2 = msub * kLog2e;
 #pragma unroll
-        for (int e = 0; e < 32; ++e) p[e] = exp2_fast((s[e] - msub) * kLog2e);
+        for (int e = 0; e < 32; ++e) x[e] = exp2_fast(__builtin_fmaf(x[e], c2, -m2));
       }
     }
     float psum = 0.f;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) psum += p[e];
+    for (int e = 0; e < 32; ++e) psum += x[e];
     l_run += psum;
 
     // ---- O^T += V^T P^T ----
 #pragma unroll
     for (int kb_ = 0; kb_ < 2; ++kb_) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int e0 = kb_ * 16 + 8 * c;
-        const u32x4 pb = {pack16x2<BF16>(p[e0], p[e0 + 1]), pack16x2<BF16>(p[e0 + 2], p[e0 + 3]),
-                          pack16x2<BF16>(p[e0 + 4], p[e0 + 5]), pack16x2<BF16>(p[e0 + 6], p[e0 + 7])};
-        const int ch = 4 * kb_ + 2 * c + hf;
+      for (int cc = 0; cc < 2; ++cc) {
+        const int e0 = kb_ * 16 + 8 * cc;
+        const u32x4 pb = {pack16x2<BF16>(x[e0], x[e0 + 1]), pack16x2<BF16>(x[e0 + 2], x[e0 + 3]),
+                          pack16x2<BF16>(x[e0 + 4], x[e0 + 5]), pack16x2<BF16>(x[e0 + 6], x[e0 + 7])};
+        const int ch = 4 * kb_ + 2 * cc + hf;
 #pragma unroll
         for (int db = 0; db < SH::ND; ++db) {
           const u32x4 vf = ld_lds16(vb + vt_off(db * 32 + lr, ch));
@@ -471,7 +499,13 @@ template <int D, int NW, bool BF16, bool E4M3, bool AD, bool X8>
 hipError_t launch_attn_one(const AttnArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)((int64_t)a.B * a.Hq * a.n_qt));
   const dim3 block(NW * 64);
-  hipLaunchKernelGGL((attn_fwd_kernel<D, NW, BF16, E4M3, AD, X8>), grid, block, 0, s, a);
+  if constexpr (!E4M3) {
+    if (a.dbg != nullptr) {
+      hipLaunchKernelGGL((attn_fwd_kernel<D, NW, BF16, E4M3, AD, X8, true>), grid, block, 0, s, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((attn_fwd_kernel<D, NW, BF16, E4M3, AD, X8, false>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
