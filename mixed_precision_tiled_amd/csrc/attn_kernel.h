@@ -40,31 +40,40 @@ struct AttnShape {
   static constexpr int NT = NW * 64;            // threads
   static constexpr int ND = D / 32;             // O^T blocks of 32 head-dim rows
   static constexpr int NQ16 = D / 16;           // 16-bit MFMAs per 32-key block
-  static constexpr int NQ8 = D / 32;            // 16-byte Q8 fragments per lane
-  static constexpr int K16_BYTES = TN * D * 2;
-  static constexpr int V_BYTES = TN * D * 2;
-  static constexpr int STAGE = K16_BYTES + V_BYTES;
-  static constexpr int CH16 = D / 8;            // 16-byte chunks per K16 row
+  static constexpr int NQ8 = D / 32;            // 16-byte Q8 / K8 fragments per lane
+  static constexpr int RB16 = 2 * D;            // bytes per K16 / V row
+  static constexpr int RB8 = D;                 // bytes per K8 row
+  static constexpr int K16_BYTES = TN * RB16;
+  static constexpr int K8_BYTES = TN * RB8;
+  static constexpr int V_BYTES = TN * RB16;
+  static constexpr int STAGE = K16_BYTES + V_BYTES;   // K region sized for K16
+  static constexpr int CH16 = D / 8;            // 16-byte chunks per K16 / V row
   static constexpr int CH8 = D / 16;            // 16-byte chunks per K8 row
-  static constexpr int M16 = (CH16 < 16 ? CH16 : 16) - 1;   // XOR swizzle masks
-  static constexpr int M8 = (CH8 < 16 ? CH8 : 16) - 1;
-  static constexpr int N_K16 = TN * CH16;       // 16-byte loads per tile
-  static constexpr int N_K8 = TN * CH8;
-  static constexpr int N_V = (TN / 4) * (D / 8);   // 4-key x 8-dim blocks per tile
-  static constexpr int LD_K16 = (N_K16 + NT - 1) / NT;
-  static constexpr int LD_K8 = (N_K8 + NT - 1) / NT;
-  static constexpr int LD_V = (N_V + NT - 1) / NT;
+  // direct-to-LDS copies: 1 KB per wave instruction, split over the waves
+  static constexpr int JK16 = K16_BYTES / 1024 / NW;
+  static constexpr int JK8 = K8_BYTES / 1024 / NW;
+  static constexpr int JV = V_BYTES / 1024 / NW;
+  static_assert(K8_BYTES % (1024 * NW) == 0, "K8 tile must split evenly over the waves");
 };
 
-// LDS byte offset of 16-byte chunk `ch` of K row `r` (row length rowbytes).
-template <int MASK>
-__device__ __forceinline__ int k_off(int r, int ch, int rowbytes) {
-  return r * rowbytes + ((ch ^ (r & MASK)) << 4);
-}
-// LDS byte offset of 16-byte chunk `ch` (0..7) of V^T row d (128 bytes/row).
-__device__ __forceinline__ int vt_off(int d, int ch) {
-  return d * 128 + ((ch ^ ((d ^ (d >> 3)) & 7)) << 4);
-}
+// LDS layouts.  Every region is row-major (one key per row) in 16-byte chunks;
+// the chunk holding logical chunk lc of row r sits at position lc ^ swz(r).
+//  * K16 / K8 rows are read by ds_read_b128 with one row per lane: swz(r)
+//    spreads the rows that share a 256-byte bank window over distinct chunk
+//    positions, so 16 consecutive rows read the same logical chunk without
+//    bank conflicts;
+//  * V rows are read by ds_read_b64_tr_b16 with four consecutive rows per
+//    16-lane group: swz(r) moves rows r..r+3 to distinct bank quads.
+template <int D>
+struct AttnSwizzle {
+  static constexpr int RP16 = 256 / (2 * D) > 1 ? 256 / (2 * D) : 1;   // rows per 256 B
+  static constexpr int M16 = (D / 8 < 16 ? D / 8 : 16) - 1;
+  static constexpr int RP8 = 256 / D > 1 ? 256 / D : 1;
+  static constexpr int M8 = (D / 16 < 16 ? D / 16 : 16) - 1;
+  __device__ static constexpr int k16(int r) { return (r / RP16) & M16; }
+  __device__ static constexpr int k8(int r) { return (r / RP8) & M8; }
+  __device__ static constexpr int v(int r) { return D == 64 ? 4 * ((r >> 1) & 1) : 4 * (r & 3); }
+};
 
 // Waves per SIMD the register budget is sized for: two for D <= 128 so that
 // one wave's MFMAs overlap the other's softmax arithmetic, one for D = 256.
@@ -83,7 +92,10 @@ void attn_fwd_kernel(const AttnArgs a) {
   // the running maximum
   constexpr bool LAZY = !ADAPTIVE && !EXP8;
   constexpr float kLogScale = LAZY ? kLog2e : 1.f;
-  __shared__ __attribute__((aligned(16))) char smem[2 * SH::STAGE];
+  // two stage buffers as distinct objects: the copy into one and the reads
+  // of the other are then provably disjoint, so reads do not wait for copies
+  __shared__ __attribute__((aligned(1024))) char smem0[SH::STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem1[SH::STAGE];
 
   // ---- workgroup -> (b, h, qt): XCD-contiguous chunks of the logical order
   //      (b, kv-head group) major, query tile descending, head minor ----
@@ -131,7 +143,7 @@ void attn_fwd_kernel(const AttnArgs a) {
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) q8[t] = ld_global16(q8p + 32 * t + 16 * hf);
   }
-  const float sQ = a.q_scale[((int64_t)b * a.Hq + h) * a.n_qt + qt];
+  const float sQ = ld_uniform(a.q_scale + ((int64_t)b * a.Hq + h) * a.n_qt + qt);
   const uint64_t* mrow = a.mask + (((int64_t)b * a.Hq + h) * a.n_qt + qt) * a.words_per_row;
 
   // per-head bases; offsets inside a head fit 32 bits (validated S <= 2^20)
@@ -144,93 +156,102 @@ void attn_fwd_kernel(const AttnArgs a) {
 
   auto tile_is8 = [&](int kt) -> bool {
     const int g = kt / a.tiles_per_bit;
-    return (mrow[g >> 6] >> (g & 63)) & 1ull;
+    return (ld_uniform(mrow + (g >> 6)) >> (g & 63)) & 1ull;
   };
 
-  // ---- global -> register staging of one key tile.  Thread mapping:
-  // K16 chunk (row kr16 + i*NT/CH16, chunk kc16), K8 likewise, V block of
-  // 4 keys (4*(vkg + i*NT/(D/8)) ...) x 8 dims (8*vdc ...) ----
-  const int kc16 = tid % SH::CH16, kr16 = tid / SH::CH16;
-  const int kc8 = tid % SH::CH8, kr8 = tid / SH::CH8;
-  const int vdc = tid % (D / 8), vkg = tid / (D / 8);
-  constexpr int R16_STEP = SH::NT / SH::CH16, R8_STEP = SH::NT / SH::CH8;
-  constexpr int VKG_STEP = SH::NT / (D / 8);
-  u32x4 kst[SH::LD_K16];
-  u32x4 vst[4 * SH::LD_V];
-  auto load_tile = [&](int kt, bool is8) {
+  // ---- direct-to-LDS staging of one key tile.  Wave w issues copies
+  // n = w + NW*j of each region; copy n fills 16-byte slots 64n .. 64n+63,
+  // slot p = (row p / CH, position p % CH) holding logical chunk
+  // position ^ swz(row).  Source offsets inside a tile are per-lane
+  // constants; a tile adds key0 * row_stride to the (uniform) base. ----
+  using SW = AttnSwizzle<D>;
+  uint32_t off_k16[SH::JK16], off_k8[SH::JK8], off_v[SH::JV];
+#pragma unroll
+  for (int j = 0; j < SH::JK16; ++j) {
+    const int p = 64 * (w + NW * j) + lane, r = p / SH::CH16;
+    off_k16[j] = (uint32_t)r * kss + (uint32_t)(((p % SH::CH16) ^ SW::k16(r)) << 4);
+  }
+#pragma unroll
+  for (int j = 0; j < SH::JK8; ++j) {
+    const int p = 64 * (w + NW * j) + lane, r = p / SH::CH8;
+    off_k8[j] = (uint32_t)(r * D + (((p % SH::CH8) ^ SW::k8(r)) << 4));
+  }
+#pragma unroll
+  for (int j = 0; j < SH::JV; ++j) {
+    const int p = 64 * (w + NW * j) + lane, r = p / SH::CH16;
+    off_v[j] = (uint32_t)r * vss + (uint32_t)(((p % SH::CH16) ^ SW::v(r)) << 4);
+  }
+  auto issue_tile = [&](int kt, bool is8, char* stage) {
+    char* kdst = stage;
+    char* vdst = stage + SH::K16_BYTES;
     const int key0 = kt * SH::TN;
-    if (is8) {
+    if (key0 + SH::TN <= a.S_k) {
+      if (is8) {
+        const uint8_t* src = k8base + (int64_t)key0 * D;
 #pragma unroll
-      for (int i = 0; i < SH::LD_K8; ++i) {
-        if (SH::N_K8 % SH::NT == 0 || tid + i * SH::NT < SH::N_K8) {
-          const int key = min(key0 + kr8 + i * R8_STEP, key_max);
-          kst[i] = ld_global16(k8base + (uint32_t)(key * D + kc8 * 16));
-        }
+        for (int j = 0; j < SH::JK8; ++j) dma16(src + off_k8[j], kdst + 1024 * (w + NW * j));
+      } else {
+        const char* src = kbase + (int64_t)key0 * kss;
+#pragma unroll
+        for (int j = 0; j < SH::JK16; ++j) dma16(src + off_k16[j], kdst + 1024 * (w + NW * j));
       }
+      const char* vsrc = vbase + (int64_t)key0 * vss;
+#pragma unroll
+      for (int j = 0; j < SH::JV; ++j) dma16(vsrc + off_v[j], vdst + 1024 * (w + NW * j));
     } else {
+      // ragged last tile: rows past S_k repeat row S_k - 1 (never valid)
+      if (is8) {
 #pragma unroll
-      for (int i = 0; i < SH::LD_K16; ++i) {
-        if (SH::N_K16 % SH::NT == 0 || tid + i * SH::NT < SH::N_K16) {
-          const int key = min(key0 + kr16 + i * R16_STEP, key_max);
-          kst[i] = ld_global16(kbase + ((uint32_t)key * kss + (uint32_t)kc16 * 16u));
+        for (int j = 0; j < SH::JK8; ++j) {
+          const int p = 64 * (w + NW * j) + lane, r = p / SH::CH8;
+          const int key = min(key0 + r, key_max);
+          dma16(k8base + (int64_t)key * D + (((p % SH::CH8) ^ SW::k8(r)) << 4),
+                kdst + 1024 * (w + NW * j));
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < SH::JK16; ++j) {
+          const int p = 64 * (w + NW * j) + lane, r = p / SH::CH16;
+          const int key = min(key0 + r, key_max);
+          dma16(kbase + (int64_t)key * kss + (((p % SH::CH16) ^ SW::k16(r)) << 4),
+                kdst + 1024 * (w + NW * j));
         }
       }
-    }
 #pragma unroll
-    for (int i = 0; i < SH::LD_V; ++i) {
-      if (SH::N_V % SH::NT == 0 || tid + i * SH::NT < SH::N_V) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = min(key0 + 4 * (vkg + i * VKG_STEP) + r, key_max);
-          vst[4 * i + r] = ld_global16(vbase + ((uint32_t)key * vss + (uint32_t)vdc * 16u));
-        }
+      for (int j = 0; j < SH::JV; ++j) {
+        const int p = 64 * (w + NW * j) + lane, r = p / SH::CH16;
+        const int key = min(key0 + r, key_max);
+        dma16(vbase + (int64_t)key * vss + (((p % SH::CH16) ^ SW::v(r)) << 4),
+              vdst + 1024 * (w + NW * j));
       }
     }
   };
-  auto store_tile = [&](int buf, bool is8) {
-    char* kb = smem + buf * SH::STAGE;
-    char* vb = kb + SH::K16_BYTES;
-    if (is8) {
+
+  // ---- per-lane LDS read offsets ----
+  // K16 fragment t of key block kb: row kb*32 + lr, logical chunk 2t + hf
+  const int s16 = SW::k16(lr), s8 = SW::k8(lr);
+  int a16[SH::NQ16], a8[SH::NQ8];
 #pragma unroll
-      for (int i = 0; i < SH::LD_K8; ++i) {
-        if (SH::N_K8 % SH::NT == 0 || tid + i * SH::NT < SH::N_K8) {
-          st_lds16(kb + k_off<SH::M8>(kr8 + i * R8_STEP, kc8, D), kst[i]);
-        }
-      }
-    } else {
+  for (int t = 0; t < SH::NQ16; ++t) a16[t] = lr * SH::RB16 + (((2 * t + hf) ^ s16) << 4);
+  // K8 fragment i: int8 logical chunk 2i + hf; e4m3 chunks 4(i/2) + 2hf + (i&1)
 #pragma unroll
-      for (int i = 0; i < SH::LD_K16; ++i) {
-        if (SH::N_K16 % SH::NT == 0 || tid + i * SH::NT < SH::N_K16) {
-          st_lds16(kb + k_off<SH::M16>(kr16 + i * R16_STEP, kc16, 2 * D), kst[i]);
-        }
-      }
+  for (int i = 0; i < SH::NQ8; ++i) {
+    const int lc = E4M3 ? 4 * (i >> 1) + 2 * hf + (i & 1) : 2 * i + hf;
+    a8[i] = lr * SH::RB8 + ((lc ^ s8) << 4);
+  }
+  // V through the transposing read: in 16-lane group g, source lane sl reads
+  // key (base + 4hf + sl/4), head dims 32db + 16(g%2) + 4(sl%4) .. +3, so that
+  // result lane l gets head dim 32db + l%32 and keys base + 4hf + 0..3
+  int av[SH::ND];
+  {
+    const int sl = lane & 15, g1 = (lane >> 4) & 1;
+    const int sv = SW::v(4 * hf + (sl >> 2));
+#pragma unroll
+    for (int db = 0; db < SH::ND; ++db) {
+      const int lc = 4 * db + 2 * g1 + ((sl & 3) >> 1);
+      av[db] = (4 * hf + (sl >> 2)) * SH::RB16 + ((lc ^ sv) << 4) + 8 * (sl & 1);
     }
-    // V: 4 keys x 8 dims per block, transposed to 8 dims x 4 keys; within a
-    // 16-key group the 4-key runs are stored in the order 0, 2, 1, 3 so that
-    // one 16-byte LDS chunk holds keys {4h..4h+3, 8+4h..8+4h+3} for h = 0, 1
-#pragma unroll
-    for (int i = 0; i < SH::LD_V; ++i) {
-      if (SH::N_V % SH::NT == 0 || tid + i * SH::NT < SH::N_V) {
-        const int kg = vkg + i * VKG_STEP;
-        const int g16 = kg >> 2, qq = kg & 3;
-        const int ch = 2 * g16 + (qq & 1), half = qq >> 1;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int d = 8 * vdc + e;
-          const int we = e >> 1;
-          uint32_t lo, hi;
-          if (e & 1) {
-            lo = (vst[4 * i + 0][we] >> 16) | (vst[4 * i + 1][we] & 0xFFFF0000u);
-            hi = (vst[4 * i + 2][we] >> 16) | (vst[4 * i + 3][we] & 0xFFFF0000u);
-          } else {
-            lo = (vst[4 * i + 0][we] & 0xFFFFu) | (vst[4 * i + 1][we] << 16);
-            hi = (vst[4 * i + 2][we] & 0xFFFFu) | (vst[4 * i + 3][we] << 16);
-          }
-          st_lds8(vb + vt_off(d, ch) + 8 * half, u32x2{lo, hi});
-        }
-      }
-    }
-  };
+  }
 
   // ---- online-softmax state of row my_row (lane-local; the two lane halves
   //      hold partial sums of l that are combined at the end) ----
@@ -252,17 +273,21 @@ void attn_fwd_kernel(const AttnArgs a) {
   auto kofs = [](int e) { return (e >> 4) * 32 + ((e & 15) >> 2) * 8 + (e & 3); };
 
   auto qk16_lds = [&](const char* kb, float* x) {
+    u32x4 kf0[SH::NQ16], kf1[SH::NQ16];
 #pragma unroll
-    for (int kb_ = 0; kb_ < 2; ++kb_) {
-      f32x16 acc = f32x16{};
-      const int r = kb_ * 32 + lr;
+    for (int t = 0; t < SH::NQ16; ++t) kf0[t] = ld_lds16(kb + a16[t]);
 #pragma unroll
-      for (int t = 0; t < SH::NQ16; ++t) {
-        const u32x4 af = ld_lds16(kb + k_off<SH::M16>(r, 2 * t + hf, 2 * D));
-        acc = mfma16<BF16>(af, q16[t], acc);
-      }
+    for (int t = 0; t < SH::NQ16; ++t) kf1[t] = ld_lds16(kb + 32 * SH::RB16 + a16[t]);
+    f32x16 acc0 = f32x16{}, acc1 = f32x16{};
 #pragma unroll
-      for (int i = 0; i < 16; ++i) x[kb_ * 16 + i] = acc[i];
+    for (int t = 0; t < SH::NQ16; ++t) {
+      acc0 = mfma16<BF16>(kf0[t], q16[t], acc0);
+      acc1 = mfma16<BF16>(kf1[t], q16[t], acc1);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      x[i] = acc0[i];
+      x[16 + i] = acc1[i];
     }
   };
   auto qk16_global = [&](int key0, float* x) {
@@ -281,45 +306,51 @@ void attn_fwd_kernel(const AttnArgs a) {
     }
   };
   auto qk8_lds = [&](const char* kb, int key0, float* x) {
+    u32x4 kf0[SH::NQ8], kf1[SH::NQ8];
 #pragma unroll
-    for (int kb_ = 0; kb_ < 2; ++kb_) {
-      const int r = kb_ * 32 + lr;
-      if constexpr (E4M3) {
-        f32x16 acc = f32x16{};
+    for (int i = 0; i < SH::NQ8; ++i) kf0[i] = ld_lds16(kb + a8[i]);
 #pragma unroll
-        for (int t = 0; t < D / 64; ++t) {
-          const u32x4 a0 = ld_lds16(kb + k_off<SH::M8>(r, 4 * t + 2 * hf, D));
-          const u32x4 a1 = ld_lds16(kb + k_off<SH::M8>(r, 4 * t + 2 * hf + 1, D));
-          acc = mfma_e4m3(a0, a1, q8[2 * t], q8[2 * t + 1], acc);
-        }
+    for (int i = 0; i < SH::NQ8; ++i) kf1[i] = ld_lds16(kb + 32 * SH::RB8 + a8[i]);
+    if constexpr (E4M3) {
+      f32x16 acc0 = f32x16{}, acc1 = f32x16{};
 #pragma unroll
-        for (int i = 0; i < 16; ++i) x[kb_ * 16 + i] = acc[i];
-      } else {
-        i32x16 acc = i32x16{};
+      for (int t = 0; t < D / 64; ++t) {
+        acc0 = mfma_e4m3(kf0[2 * t], kf0[2 * t + 1], q8[2 * t], q8[2 * t + 1], acc0);
+        acc1 = mfma_e4m3(kf1[2 * t], kf1[2 * t + 1], q8[2 * t], q8[2 * t + 1], acc1);
+      }
 #pragma unroll
-        for (int t = 0; t < D / 32; ++t) {
-          const u32x4 af = ld_lds16(kb + k_off<SH::M8>(r, 2 * t + hf, D));
-          acc = mfma_i8(af, q8[t], acc);
-        }
-        if constexpr (DBG) {
-          if (my_row < a.S_q) {
-            int32_t* dr = a.dbg + (((int64_t)b * a.Hq + h) * a.S_q + my_row) * a.S_k;
+      for (int i = 0; i < 16; ++i) {
+        x[i] = acc0[i];
+        x[16 + i] = acc1[i];
+      }
+    } else {
+      i32x16 acc[2] = {i32x16{}, i32x16{}};
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int j = key0 + kofs(kb_ * 16 + i) + 4 * hf;
-              if (j < a.S_k) dr[j] = acc[i];
-            }
+      for (int t = 0; t < D / 32; ++t) {
+        acc[0] = mfma_i8(kf0[t], q8[t], acc[0]);
+        acc[1] = mfma_i8(kf1[t], q8[t], acc[1]);
+      }
+      if constexpr (DBG) {
+        if (my_row < a.S_q) {
+          int32_t* dr = a.dbg + (((int64_t)b * a.Hq + h) * a.S_q + my_row) * a.S_k;
+#pragma unroll
+          for (int e = 0; e < 32; ++e) {
+            const int j = key0 + kofs(e) + 4 * hf;
+            if (j < a.S_k) dr[j] = acc[e >> 4][e & 15];
           }
         }
+      }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) x[kb_ * 16 + i] = (float)acc[i];
+      for (int i = 0; i < 16; ++i) {
+        x[i] = (float)acc[0][i];
+        x[16 + i] = (float)acc[1][i];
       }
     }
   };
 
-  auto compute_tile = [&](int kt, int buf, bool is8) {
-    const char* kb = smem + buf * SH::STAGE;
-    const char* vb = kb + SH::K16_BYTES;
+  auto compute_tile = [&](int kt, const char* stage, bool is8, float sK) {
+    const char* kb = stage;
+    const char* vb = stage + SH::K16_BYTES;
     const int key0 = kt * SH::TN;
     const bool need_mask = rows_ragged || (key0 + SH::TN > a.S_k) ||
                            (a.causal && key0 + SH::TN - 1 > row0);
@@ -338,7 +369,7 @@ void attn_fwd_kernel(const AttnArgs a) {
 
     if (is8) {
       qk8_lds(kb, key0, x);
-      c = (sQ * sKp[kt]) * sm * kLogScale;
+      c = (sQ * sK) * sm * kLogScale;
     } else {
       qk16_lds(kb, x);
       c = sm * kLogScale;
@@ -431,39 +462,49 @@ void attn_fwd_kernel(const AttnArgs a) {
         const int e0 = kb_ * 16 + 8 * cc;
         const u32x4 pb = {pack16x2<BF16>(x[e0], x[e0 + 1]), pack16x2<BF16>(x[e0 + 2], x[e0 + 3]),
                           pack16x2<BF16>(x[e0 + 4], x[e0 + 5]), pack16x2<BF16>(x[e0 + 6], x[e0 + 7])};
-        const int ch = 4 * kb_ + 2 * cc + hf;
+        const char* vrow = vb + (32 * kb_ + 16 * cc) * SH::RB16;
 #pragma unroll
         for (int db = 0; db < SH::ND; ++db) {
-          const u32x4 vf = ld_lds16(vb + vt_off(db * 32 + lr, ch));
-          O[db] = mfma16<BF16>(vf, pb, O[db]);
+          const u32x2 lo = ld_lds_tr16(vrow + av[db]);
+          const u32x2 hi = ld_lds_tr16(vrow + 8 * SH::RB16 + av[db]);
+          O[db] = mfma16<BF16>(u32x4{lo.x, lo.y, hi.x, hi.y}, pb, O[db]);
         }
       }
     }
   };
 
-  // ---- main loop over key tiles, ascending ----
+  // ---- main loop over key tiles, ascending.  Tile kt+1 is copied into the
+  // other buffer while tile kt is computed; the barrier at the end of a step
+  // publishes the copy and retires the buffer just read.  The loop is
+  // unrolled by two so that every access names its buffer statically. ----
   bool is8_cur = tile_is8(0);
-  load_tile(0, is8_cur);
-  store_tile(0, is8_cur);
+  float sk_cur = ld_uniform(sKp);
+  issue_tile(0, is8_cur, smem0);
+  wait_vmem();
   __syncthreads();
-  for (int kt = 0; kt < kt_end; ++kt) {
-    const int buf = kt & 1;
+  auto step = [&](int kt, const char* cur, char* nxt) {
     bool is8_next = false;
-    const bool has_next = kt + 1 < kt_end;
-    if (has_next) {
+    float sk_next = 0.f;
+    if (kt + 1 < kt_end) {
       is8_next = tile_is8(kt + 1);
-      load_tile(kt + 1, is8_next);
+      sk_next = ld_uniform(sKp + kt + 1);
+      issue_tile(kt + 1, is8_next, nxt);
     }
-    if (kt < kt_end_w) compute_tile(kt, buf, is8_cur);
-    if (has_next) store_tile(buf ^ 1, is8_next);
+    if (kt < kt_end_w) compute_tile(kt, cur, is8_cur, sk_cur);
     if constexpr (ADAPTIVE) {
       if (((kt & 63) == 63) || kt == kt_end - 1) {
         if (frow != nullptr && lane == 0) frow[kt >> 6] = fword;
         fword = 0;
       }
     }
+    wait_vmem();
     __syncthreads();
     is8_cur = is8_next;
+    sk_cur = sk_next;
+  };
+  for (int kt = 0; kt < kt_end; kt += 2) {
+    step(kt, smem0, smem1);
+    if (kt + 1 < kt_end) step(kt + 1, smem1, smem0);
   }
   if constexpr (ADAPTIVE) {
     if (frow != nullptr && lane == 0) {

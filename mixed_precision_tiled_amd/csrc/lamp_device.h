@@ -101,6 +101,34 @@ __device__ __forceinline__ u32x4 ld_lds16(const char* p) {
 __device__ __forceinline__ void st_lds16(char* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 __device__ __forceinline__ void st_lds8(char* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
 
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane i's 16 bytes land at lds_base + 16 * i, lds_base being wave-uniform.
+// Completion is tracked by vmcnt like any global load.
+__device__ __forceinline__ void dma16(const void* gsrc, char* lds_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
+                                   (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
+// Wait until every outstanding vector-memory operation of this wave (loads,
+// stores and direct-to-LDS copies) has completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// result lane 4a + j receives element j of the 8-byte reads of source lanes
+// a, a + 4, a + 8, a + 12 (in that order): a 4x4 transpose of 16-bit values.
+__device__ __forceinline__ u32x2 ld_lds_tr16(const char* p) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p);
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// Load of a wave-uniform value that nothing writes during the kernel, through
+// the constant address space: the compiler emits a scalar load.
+template <class T>
+__device__ __forceinline__ T ld_uniform(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+
 __device__ __forceinline__ float wave_swap32(float x) { return __shfl_xor(x, 32, 64); }
 
 __device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0ull; }
