@@ -1,5 +1,5 @@
 // Instantiations of the dual-path attention kernel for head dim 64.
-#include "attn_kernel.h"
+#include "attn_dispatch.h"
 
 namespace lamp {
 

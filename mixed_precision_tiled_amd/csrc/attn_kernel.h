@@ -181,50 +181,29 @@ void attn_fwd_kernel(const AttnArgs a) {
     const int p = 64 * (w + NW * j) + lane, r = p / SH::CH16;
     off_v[j] = (uint32_t)r * vss + (uint32_t)(((p % SH::CH16) ^ SW::v(r)) << 4);
   }
+  // each tile's copies go through buffer resources that start at the tile's
+  // first row and end with the head's last row: per-lane offsets past S_k
+  // (ragged last tile) fall outside the resource and read zeros, which are
+  // never valid logits
+  const uint32_t k16_bytes = (uint32_t)(a.S_k - 1) * kss + 2u * D;
+  const uint32_t k8_bytes = (uint32_t)a.S_k * D;
+  const uint32_t v_bytes = (uint32_t)(a.S_k - 1) * vss + 2u * D;
   auto issue_tile = [&](int kt, bool is8, char* stage) {
     char* kdst = stage;
     char* vdst = stage + SH::K16_BYTES;
-    const int key0 = kt * SH::TN;
-    if (key0 + SH::TN <= a.S_k) {
-      if (is8) {
-        const uint8_t* src = k8base + (int64_t)key0 * D;
+    const uint32_t key0 = (uint32_t)(kt * SH::TN);
+    if (is8) {
+      const auto rs = make_rsrc(k8base + key0 * D, k8_bytes - key0 * D);
 #pragma unroll
-        for (int j = 0; j < SH::JK8; ++j) dma16(src + off_k8[j], kdst + 1024 * (w + NW * j));
-      } else {
-        const char* src = kbase + (int64_t)key0 * kss;
-#pragma unroll
-        for (int j = 0; j < SH::JK16; ++j) dma16(src + off_k16[j], kdst + 1024 * (w + NW * j));
-      }
-      const char* vsrc = vbase + (int64_t)key0 * vss;
-#pragma unroll
-      for (int j = 0; j < SH::JV; ++j) dma16(vsrc + off_v[j], vdst + 1024 * (w + NW * j));
+      for (int j = 0; j < SH::JK8; ++j) dma16_buf(rs, off_k8[j], 0u, kdst + 1024 * (w + NW * j));
     } else {
-      // ragged last tile: rows past S_k repeat row S_k - 1 (never valid)
-      if (is8) {
+      const auto rs = make_rsrc(kbase + key0 * kss, k16_bytes - key0 * kss);
 #pragma unroll
-        for (int j = 0; j < SH::JK8; ++j) {
-          const int p = 64 * (w + NW * j) + lane, r = p / SH::CH8;
-          const int key = min(key0 + r, key_max);
-          dma16(k8base + (int64_t)key * D + (((p % SH::CH8) ^ SW::k8(r)) << 4),
-                kdst + 1024 * (w + NW * j));
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < SH::JK16; ++j) {
-          const int p = 64 * (w + NW * j) + lane, r = p / SH::CH16;
-          const int key = min(key0 + r, key_max);
-          dma16(kbase + (int64_t)key * kss + (((p % SH::CH16) ^ SW::k16(r)) << 4),
-                kdst + 1024 * (w + NW * j));
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < SH::JV; ++j) {
-        const int p = 64 * (w + NW * j) + lane, r = p / SH::CH16;
-        const int key = min(key0 + r, key_max);
-        dma16(vbase + (int64_t)key * vss + (((p % SH::CH16) ^ SW::v(r)) << 4),
-              vdst + 1024 * (w + NW * j));
-      }
+      for (int j = 0; j < SH::JK16; ++j) dma16_buf(rs, off_k16[j], 0u, kdst + 1024 * (w + NW * j));
     }
+    const auto rv = make_rsrc(vbase + key0 * vss, v_bytes - key0 * vss);
+#pragma unroll
+    for (int j = 0; j < SH::JV; ++j) dma16_buf(rv, off_v[j], 0u, vdst + 1024 * (w + NW * j));
   };
 
   // ---- per-lane LDS read offsets ----
@@ -383,7 +362,7 @@ void attn_fwd_kernel(const AttnArgs a) {
 #pragma unroll
         for (int e = 1; e < 32; ++e) mx8 = fmaxf(mx8, x[e]);
         if (!scaled) mx8 *= c;
-        mx8 = fmaxf(mx8, wave_swap32(mx8));
+        mx8 = halves_max(mx8);
         const float mprime = fmaxf(m_run, mx8);
         const bool cond = (mx8 != kNegInf) && (mx8 - mprime >= -a.tau);
         if (wave_any(cond)) {
@@ -403,7 +382,7 @@ void attn_fwd_kernel(const AttnArgs a) {
 #pragma unroll
     for (int e = 1; e < 32; ++e) mx = fmaxf(mx, x[e]);
     mx *= cm;
-    mx = fmaxf(mx, wave_swap32(mx));
+    mx = halves_max(mx);
 
     // ---- shared online-softmax update; x[] becomes p ----
     if constexpr (LAZY) {
@@ -513,7 +492,7 @@ void attn_fwd_kernel(const AttnArgs a) {
   }
 
   // ---- epilogue: O = acc / l, 16-bit store, optional LSE ----
-  const float l_tot = l_run + wave_swap32(l_run);
+  const float l_tot = halves_sum(l_run);
   if (wave_live && my_row < a.S_q) {
     const float inv_l = 1.f / l_tot;
     char* op = reinterpret_cast<char*>(a.out) +
@@ -534,39 +513,6 @@ void attn_fwd_kernel(const AttnArgs a) {
       a.lse[((int64_t)b * a.Hq + h) * a.S_q + my_row] = lse;
     }
   }
-}
-
-template <int D, int NW, bool BF16, bool E4M3, bool AD, bool X8>
-hipError_t launch_attn_one(const AttnArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)((int64_t)a.B * a.Hq * a.n_qt));
-  const dim3 block(NW * 64);
-  if constexpr (!E4M3) {
-    if (a.dbg != nullptr) {
-      hipLaunchKernelGGL((attn_fwd_kernel<D, NW, BF16, E4M3, AD, X8, true>), grid, block, 0, s, a);
-      return hipGetLastError();
-    }
-  }
-  hipLaunchKernelGGL((attn_fwd_kernel<D, NW, BF16, E4M3, AD, X8, false>), grid, block, 0, s, a);
-  return hipGetLastError();
-}
-
-template <int D, int NW, bool BF16, bool E4M3, bool AD>
-hipError_t dispatch_x8(const AttnArgs& a, const AttnConfig& c, hipStream_t s) {
-  return c.exp8 ? launch_attn_one<D, NW, BF16, E4M3, AD, true>(a, s)
-                : launch_attn_one<D, NW, BF16, E4M3, AD, false>(a, s);
-}
-template <int D, int NW, bool BF16, bool E4M3>
-hipError_t dispatch_ad(const AttnArgs& a, const AttnConfig& c, hipStream_t s) {
-  return c.adaptive ? dispatch_x8<D, NW, BF16, E4M3, true>(a, c, s)
-                    : dispatch_x8<D, NW, BF16, E4M3, false>(a, c, s);
-}
-template <int D, int NW, bool BF16>
-hipError_t dispatch_code(const AttnArgs& a, const AttnConfig& c, hipStream_t s) {
-  return c.e4m3 ? dispatch_ad<D, NW, BF16, true>(a, c, s) : dispatch_ad<D, NW, BF16, false>(a, c, s);
-}
-template <int D, int NW>
-hipError_t dispatch_dtype(const AttnArgs& a, const AttnConfig& c, hipStream_t s) {
-  return c.bf16 ? dispatch_code<D, NW, true>(a, c, s) : dispatch_code<D, NW, false>(a, c, s);
 }
 
 }  // namespace lamp

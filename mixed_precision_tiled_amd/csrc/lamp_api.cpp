@@ -187,6 +187,9 @@ lamp_status lamp_attn_fwd(const lamp_attn_params* p, void* stream) {
   if (p->flags_out && (reinterpret_cast<uintptr_t>(p->flags_out) & 7u))
     return fail(LAMP_ERR_ALIGN, "flags_out alignment");
   if (p->B * p->Hq * n_qt > kMaxGrid) return fail(LAMP_ERR_UNSUPPORTED, "grid too large");
+  // K and V rows of one head are addressed with 32-bit byte offsets
+  if (2 * p->S_k * p->k_str[2] >= (int64_t(1) << 31) || 2 * p->S_k * p->v_str[2] >= (int64_t(1) << 31))
+    return fail(LAMP_ERR_UNSUPPORTED, "K/V rows of one head span 2 GiB or more");
 
   lamp::AttnArgs a{};
   a.q = p->q;

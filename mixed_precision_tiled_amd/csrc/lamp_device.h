@@ -129,7 +129,31 @@ __device__ __forceinline__ T ld_uniform(const T* p) {
   return *(const __attribute__((address_space(4))) T*)p;
 }
 
-__device__ __forceinline__ float wave_swap32(float x) { return __shfl_xor(x, 32, 64); }
+// x of the lane in the other 32-lane half (lane l gets x[l ^ 32]).
+// v_permlane32_swap exchanges the upper half of its first operand with the
+// lower half of its second; with x in both operands the lower-half lanes
+// find x[l + 32] in the second result and the upper-half lanes x[l - 32] in
+// the first, whether or not the compiler gives both operands one register.
+__device__ __forceinline__ float other_half(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto pr = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (__lane_id() & 32) ? pr[0] : pr[1]);
+}
+__device__ __forceinline__ float halves_max(float x) { return fmaxf(x, other_half(x)); }
+__device__ __forceinline__ float halves_sum(float x) { return x + other_half(x); }
+
+// Raw buffer resource over [base, base + bytes): buffer loads at offsets at
+// or beyond `bytes` return zeros instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// Direct buffer -> LDS copy of 16 bytes per lane at byte offset voff + soff;
+// lane i's bytes land at lds_base + 16 * i.
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                          char* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16,
+                                           voff, soff, 0, 0);
+}
 
 __device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0ull; }
 
