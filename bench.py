@@ -35,6 +35,7 @@ PEAK8 = 5.0e15      # MI355X dense int8 / fp8 MFMA, ops/s
 PEAK16 = 2.5e15     # MI355X dense bf16 / fp16 MFMA, flop/s
 KERNEL_SOURCES = ["mixed_precision_tiled_amd/csrc/attn_kernel.h",
                   "mixed_precision_tiled_amd/csrc/lamp_device.h",
+                  "mixed_precision_tiled_amd/csrc/attn_dispatch.h",
                   "mixed_precision_tiled_amd/csrc/attn_d64.hip",
                   "mixed_precision_tiled_amd/csrc/attn_d128.hip",
                   "mixed_precision_tiled_amd/csrc/attn_d256.hip"]
@@ -228,13 +229,16 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="C5", choices=["C1", "C2", "C3", "C4", "C5"])
     ap.add_argument("--frac", type=float, default=None, help="C5: 16-bit fraction")
     ap.add_argument("--code", default=None, choices=["i8", "e4m3"], help="C5: 8-bit code")
     ap.add_argument("--no-sweep", action="store_true", help="skip the C5 precision-mix sweep")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after the run, copy MIB MiB device-to-device once (reference "
+                         "dispatch for scaling the HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -340,6 +344,15 @@ def main():
         result["cpu_baseline"] = cpu_baseline(cfg, q, k, v, budget_s=args.cpu_budget)
     else:
         result["cpu_baseline"] = None
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: {n} bytes read + {n} bytes written")
+        del src, dst
     print(json.dumps(result), flush=True)
 
 
