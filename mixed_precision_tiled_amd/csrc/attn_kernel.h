@@ -284,6 +284,10 @@ void attn_fwd_kernel(const AttnArgs a) {
       for (int i = 0; i < 16; ++i) x[kb_ * 16 + i] = acc[i];
     }
   };
+  // int8 accumulator start value, kept in registers across the loop
+  i32x16 acc_init;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc_init[i] = LAZY ? kMagicBits : 0;
   auto qk8_lds = [&](const char* kb, int key0, float* x) {
     u32x4 kf0[SH::NQ8], kf1[SH::NQ8];
 #pragma unroll
@@ -297,15 +301,23 @@ void attn_fwd_kernel(const AttnArgs a) {
         acc0 = mfma_e4m3(kf0[2 * t], kf0[2 * t + 1], q8[2 * t], q8[2 * t + 1], acc0);
         acc1 = mfma_e4m3(kf1[2 * t], kf1[2 * t + 1], q8[2 * t], q8[2 * t + 1], acc1);
       }
+      xdl16_settle();
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         x[i] = acc0[i];
         x[16 + i] = acc1[i];
       }
     } else {
-      i32x16 acc[2] = {i32x16{}, i32x16{}};
+      // LAZY: the accumulator starts at the bits of the float 1.5 * 2^23, so
+      // that its result bits are the float 1.5 * 2^23 + acc (exact: |acc| <=
+      // 256 * 127^2 < 2^22), and no int -> float conversion is needed;
+      // callers subtract kMagic.  Otherwise plain integers, converted.
+      const int init = LAZY ? kMagicBits : 0;
+      i32x16 acc[2];
+      acc[0] = mfma_i8(kf0[0], q8[0], acc_init);
+      acc[1] = mfma_i8(kf1[0], q8[0], acc_init);
 #pragma unroll
-      for (int t = 0; t < D / 32; ++t) {
+      for (int t = 1; t < D / 32; ++t) {
         acc[0] = mfma_i8(kf0[t], q8[t], acc[0]);
         acc[1] = mfma_i8(kf1[t], q8[t], acc[1]);
       }
@@ -315,14 +327,22 @@ void attn_fwd_kernel(const AttnArgs a) {
 #pragma unroll
           for (int e = 0; e < 32; ++e) {
             const int j = key0 + kofs(e) + 4 * hf;
-            if (j < a.S_k) dr[j] = acc[e >> 4][e & 15];
+            if (j < a.S_k) dr[j] = acc[e >> 4][e & 15] - init;
           }
         }
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        x[i] = (float)acc[0][i];
-        x[16 + i] = (float)acc[1][i];
+        if constexpr (LAZY) {
+          // bit-cast from scalar copies: hipcc mistranslates a bit cast
+          // applied directly to a vector-element lvalue (it reads element 0)
+          const int v0 = acc[0][i], v1 = acc[1][i];
+          x[i] = __builtin_bit_cast(float, v0);
+          x[16 + i] = __builtin_bit_cast(float, v1);
+        } else {
+          x[i] = (float)acc[0][i];
+          x[16 + i] = (float)acc[1][i];
+        }
       }
     }
   };
@@ -336,19 +356,22 @@ void attn_fwd_kernel(const AttnArgs a) {
     // valid(e) <=> kofs(e) <= lim_rel
     const int lim_rel = key_lim - key0 - 4 * hf;
     float x[32];
-    float c;                 // logit = x * c (base-2 units when LAZY)
+    float c;                 // logit = (x - xoff) * c (base-2 units when LAZY)
+    float xoff = 0.f;
     bool is16 = !is8;
-    bool scaled = false;     // x already holds c * x with invalid entries -inf
+    bool scaled = false;     // x already holds the logits, invalid entries -inf
 
     auto mask_scale = [&]() {
 #pragma unroll
-      for (int e = 0; e < 32; ++e) x[e] = kofs(e) <= lim_rel ? x[e] * c : kNegInf;
+      for (int e = 0; e < 32; ++e) x[e] = kofs(e) <= lim_rel ? (x[e] - xoff) * c : kNegInf;
+      xoff = 0.f;
       scaled = true;
     };
 
     if (is8) {
       qk8_lds(kb, key0, x);
       c = (sQ * sK) * sm * kLogScale;
+      if constexpr (LAZY && !E4M3) xoff = kMagic;
     } else {
       qk16_lds(kb, x);
       c = sm * kLogScale;
@@ -381,7 +404,7 @@ void attn_fwd_kernel(const AttnArgs a) {
     float mx = x[0];
 #pragma unroll
     for (int e = 1; e < 32; ++e) mx = fmaxf(mx, x[e]);
-    mx *= cm;
+    mx = (mx - xoff) * cm;
     mx = halves_max(mx);
 
     // ---- shared online-softmax update; x[] becomes p ----
@@ -396,7 +419,8 @@ void attn_fwd_kernel(const AttnArgs a) {
         for (int db = 0; db < SH::ND; ++db) O[db] *= alpha;
         m_run = m_new;
       }
-      const float msub = (m_run == kNegInf) ? 0.f : m_run;
+      // exp2((x - xoff) * cm - m) with the offset folded into the constant
+      const float msub = ((m_run == kNegInf) ? 0.f : m_run) + xoff * cm;
 #pragma unroll
       for (int e = 0; e < 32; ++e) x[e] = exp2_fast(__builtin_fmaf(x[e], cm, -msub));
     } else {
@@ -428,19 +452,26 @@ void attn_fwd_kernel(const AttnArgs a) {
         for (int e = 0; e < 32; ++e) x[e] = exp2_fast(__builtin_fmaf(x[e], c2, -m2));
       }
     }
-    float psum = 0.f;
+    // ---- p to 16 bits (the B operand of P V); the normaliser sums exactly
+    //      these rounded weights, two at a time (dot2 with (1, 1)) ----
+    uint32_t pk[16];
 #pragma unroll
-    for (int e = 0; e < 32; ++e) psum += x[e];
-    l_run += psum;
+    for (int i = 0; i < 16; ++i) pk[i] = pack16x2<BF16>(x[2 * i], x[2 * i + 1]);
+    float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      ps0 = sum16x2<BF16>(pk[i], ps0);
+      ps1 = sum16x2<BF16>(pk[i + 1], ps1);
+    }
+    l_run += ps0 + ps1;
 
     // ---- O^T += V^T P^T ----
 #pragma unroll
     for (int kb_ = 0; kb_ < 2; ++kb_) {
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
-        const int e0 = kb_ * 16 + 8 * cc;
-        const u32x4 pb = {pack16x2<BF16>(x[e0], x[e0 + 1]), pack16x2<BF16>(x[e0 + 2], x[e0 + 3]),
-                          pack16x2<BF16>(x[e0 + 4], x[e0 + 5]), pack16x2<BF16>(x[e0 + 6], x[e0 + 7])};
+        const int i0 = kb_ * 8 + 4 * cc;
+        const u32x4 pb = {pk[i0], pk[i0 + 1], pk[i0 + 2], pk[i0 + 3]};
         const char* vrow = vb + (32 * kb_ + 16 * cc) * SH::RB16;
 #pragma unroll
         for (int db = 0; db < SH::ND; ++db) {

@@ -45,6 +45,17 @@ __device__ __forceinline__ i32x16 mfma_i8(u32x4 a, u32x4 b, i32x16 c) {
                                                __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
 }
 
+// Wait states after the last v_mfma_scale_f32_32x32x64_f8f6f4 of a chain
+// before its result is read.  With fp8 operands the instruction takes 16
+// passes; hipcc (ROCm 7.2) lets a v_accvgpr_read of the result follow 12
+// wait states after it, which returned stale accumulator values on MI355X.
+// The scheduling barriers keep every read behind the 20 explicit wait states.
+__device__ __forceinline__ void xdl16_settle() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 15\n\ts_nop 3");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // OCP e4m3 x e4m3, K = 64, unit block scales (E8M0 127 = 2^0).
 __device__ __forceinline__ f32x16 mfma_e4m3(u32x4 a0, u32x4 a1, u32x4 b0, u32x4 b1, f32x16 c) {
   i32x8 a = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
@@ -86,6 +97,24 @@ __device__ __forceinline__ float from16(uint32_t bits16) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
   }
 }
+
+// c + lo + hi of two packed 16-bit values (v_dot2c_f32_{bf16,f16} with the
+// multiplier pair (1, 1): the products are exact).
+template <bool BF16>
+__device__ __forceinline__ float sum16x2(uint32_t v, float c) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v),
+                                           __builtin_bit_cast(bf16x2, 0x3F803F80u), c, false);
+  } else {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, v), __builtin_bit_cast(f16x2, 0x3C003C00u),
+                                  c, false);
+  }
+}
+
+// int32 accumulators started at kMagicBits hold the float kMagic + acc for
+// |acc| < 2^22 (floats in [2^23, 2^24) have unit spacing).
+constexpr int kMagicBits = 0x4B400000;
+constexpr float kMagic = 12582912.0f;   // 1.5 * 2^23
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -137,7 +166,8 @@ __device__ __forceinline__ T ld_uniform(const T* p) {
 __device__ __forceinline__ float other_half(float x) {
   const unsigned u = __builtin_bit_cast(unsigned, x);
   const auto pr = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return __builtin_bit_cast(float, (__lane_id() & 32) ? pr[0] : pr[1]);
+  const unsigned r = (__lane_id() & 32) ? pr[0] : pr[1];
+  return __builtin_bit_cast(float, r);
 }
 __device__ __forceinline__ float halves_max(float x) { return fmaxf(x, other_half(x)); }
 __device__ __forceinline__ float halves_sum(float x) { return x + other_half(x); }

@@ -86,9 +86,13 @@ def check_head(cfg, P, g, b, h, rows=None, sub_blocks=None, report=None):
         lse_rows = rr
     assert st["ok"], f"head ({b},{h}): {st}"
     if g["lse"] is not None:
+        # the kernel's normaliser sums the 16-bit-rounded weights that also
+        # feed P V, so its log can be off by ln(1 + u16) (u16 = 2^-8 for
+        # bf16, 2^-11 for fp16) on top of fp32 rounding
+        u16 = 2.0 ** -8 if cfg.dtype == "bf16" else 2.0 ** -11
         lg = g["lse"][b, h][lse_rows]
         assert np.isfinite(lg).all()
-        assert np.abs(lg - lse_ref).max() <= 1e-3 + 1e-5 * np.abs(lse_ref).max() + (
+        assert np.abs(lg - lse_ref).max() <= 1e-3 + u16 + 1e-5 * np.abs(lse_ref).max() + (
             0.05 if A.uses_lamp(P) else 0.0)
     return st
 
