@@ -28,6 +28,8 @@
 //     (shared K/V in its L2), longest causal query tiles first.
 #pragma once
 
+#include <type_traits>
+
 #include "lamp_device.h"
 #include "lamp_internal.h"
 
@@ -92,10 +94,13 @@ void attn_fwd_kernel(const AttnArgs a) {
   // the running maximum
   constexpr bool LAZY = !ADAPTIVE && !EXP8;
   constexpr float kLogScale = LAZY ? kLog2e : 1.f;
-  // two stage buffers as distinct objects: the copy into one and the reads
-  // of the other are then provably disjoint, so reads do not wait for copies
-  __shared__ __attribute__((aligned(1024))) char smem0[SH::STAGE];
-  __shared__ __attribute__((aligned(1024))) char smem1[SH::STAGE];
+  // double-buffered K and V tiles as four distinct objects: copies into one
+  // buffer and reads of another are then provably disjoint, so reads do not
+  // wait for copies in flight
+  __shared__ __attribute__((aligned(1024))) char sk0[SH::K16_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sk1[SH::K16_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sv0[SH::V_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sv1[SH::V_BYTES];
 
   // ---- workgroup -> (b, h, qt): XCD-contiguous chunks of the logical order
   //      (b, kv-head group) major, query tile descending, head minor ----
@@ -188,9 +193,7 @@ void attn_fwd_kernel(const AttnArgs a) {
   const uint32_t k16_bytes = (uint32_t)(a.S_k - 1) * kss + 2u * D;
   const uint32_t k8_bytes = (uint32_t)a.S_k * D;
   const uint32_t v_bytes = (uint32_t)(a.S_k - 1) * vss + 2u * D;
-  auto issue_tile = [&](int kt, bool is8, char* stage) {
-    char* kdst = stage;
-    char* vdst = stage + SH::K16_BYTES;
+  auto issue_k = [&](int kt, bool is8, char* kdst) {
     const uint32_t key0 = (uint32_t)(kt * SH::TN);
     if (is8) {
       const auto rs = make_rsrc(k8base + key0 * D, k8_bytes - key0 * D);
@@ -201,6 +204,9 @@ void attn_fwd_kernel(const AttnArgs a) {
 #pragma unroll
       for (int j = 0; j < SH::JK16; ++j) dma16_buf(rs, off_k16[j], 0u, kdst + 1024 * (w + NW * j));
     }
+  };
+  auto issue_v = [&](int kt, char* vdst) {
+    const uint32_t key0 = (uint32_t)(kt * SH::TN);
     const auto rv = make_rsrc(vbase + key0 * vss, v_bytes - key0 * vss);
 #pragma unroll
     for (int j = 0; j < SH::JV; ++j) dma16_buf(rv, off_v[j], 0u, vdst + 1024 * (w + NW * j));
@@ -347,34 +353,37 @@ void attn_fwd_kernel(const AttnArgs a) {
     }
   };
 
-  auto compute_tile = [&](int kt, const char* stage, bool is8, float sK) {
-    const char* kb = stage;
-    const char* vb = stage + SH::K16_BYTES;
+  // ---- one key tile, split in three parts so that a wave can overlap the
+  //      P V products of tile kt-1 with the softmax of tile kt ----
+  // (1) logits of tile kt: x = raw scores, logit = (x - xoff) * c, or the
+  //     logits themselves (scaled) with invalid entries -inf
+  struct Logits {
+    float c, xoff;
+    bool is16, scaled;
+  };
+  auto qk_part = [&](int kt, const char* kb, bool is8, float sK, float* x) -> Logits {
     const int key0 = kt * SH::TN;
     const bool need_mask = rows_ragged || (key0 + SH::TN > a.S_k) ||
                            (a.causal && key0 + SH::TN - 1 > row0);
     // valid(e) <=> kofs(e) <= lim_rel
     const int lim_rel = key_lim - key0 - 4 * hf;
-    float x[32];
-    float c;                 // logit = (x - xoff) * c (base-2 units when LAZY)
-    float xoff = 0.f;
-    bool is16 = !is8;
-    bool scaled = false;     // x already holds the logits, invalid entries -inf
-
+    Logits lg;
+    lg.xoff = 0.f;
+    lg.is16 = !is8;
+    lg.scaled = false;
     auto mask_scale = [&]() {
 #pragma unroll
-      for (int e = 0; e < 32; ++e) x[e] = kofs(e) <= lim_rel ? (x[e] - xoff) * c : kNegInf;
-      xoff = 0.f;
-      scaled = true;
+      for (int e = 0; e < 32; ++e) x[e] = kofs(e) <= lim_rel ? (x[e] - lg.xoff) * lg.c : kNegInf;
+      lg.xoff = 0.f;
+      lg.scaled = true;
     };
-
     if (is8) {
       qk8_lds(kb, key0, x);
-      c = (sQ * sK) * sm * kLogScale;
-      if constexpr (LAZY && !E4M3) xoff = kMagic;
+      lg.c = (sQ * sK) * sm * kLogScale;
+      if constexpr (LAZY && !E4M3) lg.xoff = kMagic;
     } else {
       qk16_lds(kb, x);
-      c = sm * kLogScale;
+      lg.c = sm * kLogScale;
     }
     if (need_mask) mask_scale();
     if constexpr (ADAPTIVE) {
@@ -384,88 +393,27 @@ void attn_fwd_kernel(const AttnArgs a) {
         float mx8 = x[0];
 #pragma unroll
         for (int e = 1; e < 32; ++e) mx8 = fmaxf(mx8, x[e]);
-        if (!scaled) mx8 *= c;
+        if (!lg.scaled) mx8 *= lg.c;
         mx8 = halves_max(mx8);
         const float mprime = fmaxf(m_run, mx8);
         const bool cond = (mx8 != kNegInf) && (mx8 - mprime >= -a.tau);
         if (wave_any(cond)) {
-          is16 = true;
+          lg.is16 = true;
           fword |= 1ull << (kt & 63);
           // recompute the sub-block's logits at 16 bits, K16 straight from
           // global memory (only flagged sub-blocks need it)
           qk16_global(key0, x);
-          c = sm;
-          scaled = false;
+          lg.c = sm;
+          lg.scaled = false;
           if (need_mask) mask_scale();
         }
       }
     }
-    const float cm = scaled ? 1.f : c;
-    float mx = x[0];
-#pragma unroll
-    for (int e = 1; e < 32; ++e) mx = fmaxf(mx, x[e]);
-    mx = (mx - xoff) * cm;
-    mx = halves_max(mx);
+    return lg;
+  };
 
-    // ---- shared online-softmax update; x[] becomes p ----
-    if constexpr (LAZY) {
-      // the reference maximum only moves when a row's max grows by more
-      // than 8 (so p <= 2^8 in between)
-      if (wave_any(mx > m_run + 8.f)) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = (m_new == kNegInf) ? 1.f : exp2_fast(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < SH::ND; ++db) O[db] *= alpha;
-        m_run = m_new;
-      }
-      // exp2((x - xoff) * cm - m) with the offset folded into the constant
-      const float msub = ((m_run == kNegInf) ? 0.f : m_run) + xoff * cm;
-#pragma unroll
-      for (int e = 0; e < 32; ++e) x[e] = exp2_fast(__builtin_fmaf(x[e], cm, -msub));
-    } else {
-      const float m_new = fmaxf(m_run, mx);
-      if (wave_any(m_new != m_run)) {
-        const float alpha = (m_run == kNegInf) ? 0.f : exp2_fast((m_run - m_new) * kLog2e);
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < SH::ND; ++db) O[db] *= alpha;
-        m_run = m_new;
-      }
-      const float msub = (m_run == kNegInf) ? 0.f : m_run;
-      if (EXP8 && !is16) {
-        // x = s - m rounded to e4m3, exp, rounded to e4m3 again
-#pragma unroll
-        for (int e = 0; e < 32; e += 2) {
-          const float x0 = fmaxf(__builtin_fmaf(x[e], cm, -msub), -448.f);
-          const float x1 = fmaxf(__builtin_fmaf(x[e + 1], cm, -msub), -448.f);
-          const f32x2 xq = e4m3x2_to_f32(f32x2_to_e4m3(x0, x1));
-          const float e0 = exp2_fast(xq.x * kLog2e);
-          const float e1 = exp2_fast(xq.y * kLog2e);
-          const f32x2 pq = e4m3x2_to_f32(f32x2_to_e4m3(e0, e1));
-          x[e] = pq.x;
-          x[e + 1] = pq.y;
-        }
-      } else {
-        const float c2 = cm * kLog2e, m2 = msub * kLog2e;
-#pragma unroll
-        for (int e = 0; e < 32; ++e) x[e] = exp2_fast(__builtin_fmaf(x[e], c2, -m2));
-      }
-    }
-    // ---- p to 16 bits (the B operand of P V); the normaliser sums exactly
-    //      these rounded weights, two at a time (dot2 with (1, 1)) ----
-    uint32_t pk[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) pk[i] = pack16x2<BF16>(x[2 * i], x[2 * i + 1]);
-    float ps0 = 0.f, ps1 = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; i += 2) {
-      ps0 = sum16x2<BF16>(pk[i], ps0);
-      ps1 = sum16x2<BF16>(pk[i + 1], ps1);
-    }
-    l_run += ps0 + ps1;
-
-    // ---- O^T += V^T P^T ----
+  // (2) O^T += V^T P^T for a tile whose 16-bit weights are pk
+  auto pv_part = [&](const char* vb, const uint32_t* pk) {
 #pragma unroll
     for (int kb_ = 0; kb_ < 2; ++kb_) {
 #pragma unroll
@@ -483,24 +431,143 @@ void attn_fwd_kernel(const AttnArgs a) {
     }
   };
 
-  // ---- main loop over key tiles, ascending.  Tile kt+1 is copied into the
-  // other buffer while tile kt is computed; the barrier at the end of a step
-  // publishes the copy and retires the buffer just read.  The loop is
+  // Instruction order for the block holding P V of tile kt-1 and the
+  // softmax of tile kt: a wave issues in order and an MFMA waits for the
+  // matrix pipe, so the 16 MFMAs are spread over the softmax arithmetic
+  // (V reads a few MFMAs ahead) instead of being issued back to back.
+  auto interleave_pv_softmax = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);   // 6 LDS reads
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // 8 VALU
+    }
+  };
+
+  // (3) shared online-softmax update with the logits of tile kt; writes the
+  //     16-bit weights to pk.  Any rescale of O applies to everything
+  //     accumulated so far, P V of the previous tile included.
+  auto softmax_part = [&](float* x, const Logits& lg, uint32_t* pk) {
+    const float cm = lg.scaled ? 1.f : lg.c;
+    const float xoff = lg.xoff;
+    float mx = x[0];
+#pragma unroll
+    for (int e = 1; e < 32; ++e) mx = fmaxf(mx, x[e]);
+    mx = (mx - xoff) * cm;
+    mx = halves_max(mx);
+    float xs[32];
+    auto weights = [&](float mref) {
+      if constexpr (LAZY) {
+        // exp2((x - xoff) * cm - m) with the offset folded into the constant
+        const float msub = ((mref == kNegInf) ? 0.f : mref) + xoff * cm;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) xs[e] = exp2_fast(__builtin_fmaf(x[e], cm, -msub));
+      } else {
+        const float msub = (mref == kNegInf) ? 0.f : mref;
+        if (EXP8 && !lg.is16) {
+          // x = s - m rounded to e4m3, exp, rounded to e4m3 again
+#pragma unroll
+          for (int e = 0; e < 32; e += 2) {
+            const float x0 = fmaxf(__builtin_fmaf(x[e], cm, -msub), -448.f);
+            const float x1 = fmaxf(__builtin_fmaf(x[e + 1], cm, -msub), -448.f);
+            const f32x2 xq = e4m3x2_to_f32(f32x2_to_e4m3(x0, x1));
+            const float e0 = exp2_fast(xq.x * kLog2e);
+            const float e1 = exp2_fast(xq.y * kLog2e);
+            const f32x2 pq = e4m3x2_to_f32(f32x2_to_e4m3(e0, e1));
+            xs[e] = pq.x;
+            xs[e + 1] = pq.y;
+          }
+        } else {
+          const float c2 = cm * kLog2e, m2 = msub * kLog2e;
+#pragma unroll
+          for (int e = 0; e < 32; ++e) xs[e] = exp2_fast(__builtin_fmaf(x[e], c2, -m2));
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pk[i] = pack16x2<BF16>(xs[2 * i], xs[2 * i + 1]);
+    };
+    auto psum = [&]() {
+      // the normaliser sums exactly the rounded weights that feed P V
+      float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        ps0 = sum16x2<BF16>(pk[i], ps0);
+        ps1 = sum16x2<BF16>(pk[i + 1], ps1);
+      }
+      return ps0 + ps1;
+    };
+    if constexpr (LAZY) {
+      // the reference maximum only moves when a row's max grows by more
+      // than 8 (so p <= 2^8 in between).  The weights are computed for the
+      // current reference first, in the same basic block as the P V
+      // products issued before them (the empty asm keeps them from being
+      // sunk into the branch), and recomputed in the rare case it moves.
+      weights(m_run);
+      float l_add = psum();
+      asm volatile("" : "+v"(l_add));
+      interleave_pv_softmax();
+      if (wave_any(mx > m_run + 8.f)) {
+        __builtin_amdgcn_sched_barrier(0);
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = (m_new == kNegInf) ? 1.f : exp2_fast(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < SH::ND; ++db) O[db] *= alpha;
+        m_run = m_new;
+        weights(m_run);
+        l_add = psum();
+      }
+      l_run += l_add;
+    } else {
+      // exact running maximum: the weights use it directly
+      const float m_new = fmaxf(m_run, mx);
+      weights(m_new);
+      const float alpha = (m_run == kNegInf) ? 0.f : exp2_fast((m_run - m_new) * kLog2e);
+      l_run = __builtin_fmaf(l_run, alpha, psum());
+      interleave_pv_softmax();
+      if (wave_any(m_new != m_run)) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int db = 0; db < SH::ND; ++db) O[db] *= alpha;
+      }
+      m_run = m_new;
+    }
+  };
+
+  // ---- main loop over key tiles, ascending.  Step kt computes the logits
+  // of tile kt (K from one K buffer), P V of tile kt-1 (V from one V
+  // buffer) and the softmax of tile kt, while K of tile kt+1 and V of tile
+  // kt are copied into the other buffers; the barrier at the end of a step
+  // publishes the copies and retires the buffers just read.  The loop is
   // unrolled by two so that every access names its buffer statically. ----
+  uint32_t pk[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) pk[i] = 0u;
   bool is8_cur = tile_is8(0);
   float sk_cur = ld_uniform(sKp);
-  issue_tile(0, is8_cur, smem0);
+  issue_k(0, is8_cur, sk0);
   wait_vmem();
   __syncthreads();
-  auto step = [&](int kt, const char* cur, char* nxt) {
+  // FIRST: tile 0, which has no previous tile to multiply with V
+  auto step = [&](auto first, int kt, const char* kcur, char* knxt, const char* vprev, char* vcur) {
+    constexpr bool FIRST = decltype(first)::value;
     bool is8_next = false;
     float sk_next = 0.f;
     if (kt + 1 < kt_end) {
       is8_next = tile_is8(kt + 1);
       sk_next = ld_uniform(sKp + kt + 1);
-      issue_tile(kt + 1, is8_next, nxt);
+      issue_k(kt + 1, is8_next, knxt);
     }
-    if (kt < kt_end_w) compute_tile(kt, cur, is8_cur, sk_cur);
+    issue_v(kt, vcur);
+    if (kt < kt_end_w) {
+      float x[32];
+      const Logits lg = qk_part(kt, kcur, is8_cur, sk_cur, x);
+      if constexpr (!FIRST) pv_part(vprev, pk);
+      softmax_part(x, lg, pk);
+    } else if (!FIRST && kt - 1 < kt_end_w) {
+      pv_part(vprev, pk);
+    }
     if constexpr (ADAPTIVE) {
       if (((kt & 63) == 63) || kt == kt_end - 1) {
         if (frow != nullptr && lane == 0) frow[kt >> 6] = fword;
@@ -512,16 +579,23 @@ void attn_fwd_kernel(const AttnArgs a) {
     is8_cur = is8_next;
     sk_cur = sk_next;
   };
-  for (int kt = 0; kt < kt_end; kt += 2) {
-    step(kt, smem0, smem1);
-    if (kt + 1 < kt_end) step(kt + 1, smem1, smem0);
+  using True_ = std::integral_constant<bool, true>;
+  using False_ = std::integral_constant<bool, false>;
+  if (kt_end > 0) step(True_{}, 0, sk0, sk1, sv1, sv0);
+  for (int kt = 1; kt < kt_end; kt += 2) {
+    step(False_{}, kt, sk1, sk0, sv0, sv1);
+    if (kt + 1 < kt_end) step(False_{}, kt + 1, sk0, sk1, sv1, sv0);
+  }
+  // P V of the last tile (its V was copied in the last step)
+  if (kt_end_w == kt_end && kt_end > 0) {
+    if ((kt_end - 1) & 1) pv_part(sv1, pk);
+    else pv_part(sv0, pk);
   }
   if constexpr (ADAPTIVE) {
     if (frow != nullptr && lane == 0) {
       for (int wd = ((kt_end - 1) >> 6) + 1; wd < a.flag_words; ++wd) frow[wd] = 0;
     }
   }
-
   // ---- epilogue: O = acc / l, 16-bit store, optional LSE ----
   const float l_tot = halves_sum(l_run);
   if (wave_live && my_row < a.S_q) {
