@@ -436,12 +436,14 @@ void attn_fwd_kernel(const AttnArgs a) {
   // matrix pipe, so the 16 MFMAs are spread over the softmax arithmetic
   // (V reads a few MFMAs ahead) instead of being issued back to back.
   auto interleave_pv_softmax = [&]() {
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);   // 6 LDS reads
+    constexpr int NMF = 4 * SH::ND;                        // P V MFMAs per tile
+    constexpr int NVALU = D >= 256 ? 4 : (D == 64 ? 16 : 8);
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);     // 6 LDS reads
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < NMF; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 LDS reads
-      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // 8 VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, NVALU, 0);   // VALU
     }
   };
 
@@ -456,13 +458,13 @@ void attn_fwd_kernel(const AttnArgs a) {
     for (int e = 1; e < 32; ++e) mx = fmaxf(mx, x[e]);
     mx = (mx - xoff) * cm;
     mx = halves_max(mx);
-    float xs[32];
+    // the weights overwrite x in place
     auto weights = [&](float mref) {
       if constexpr (LAZY) {
         // exp2((x - xoff) * cm - m) with the offset folded into the constant
         const float msub = ((mref == kNegInf) ? 0.f : mref) + xoff * cm;
 #pragma unroll
-        for (int e = 0; e < 32; ++e) xs[e] = exp2_fast(__builtin_fmaf(x[e], cm, -msub));
+        for (int e = 0; e < 32; ++e) x[e] = exp2_fast(__builtin_fmaf(x[e], cm, -msub));
       } else {
         const float msub = (mref == kNegInf) ? 0.f : mref;
         if (EXP8 && !lg.is16) {
@@ -475,17 +477,17 @@ void attn_fwd_kernel(const AttnArgs a) {
             const float e0 = exp2_fast(xq.x * kLog2e);
             const float e1 = exp2_fast(xq.y * kLog2e);
             const f32x2 pq = e4m3x2_to_f32(f32x2_to_e4m3(e0, e1));
-            xs[e] = pq.x;
-            xs[e + 1] = pq.y;
+            x[e] = pq.x;
+            x[e + 1] = pq.y;
           }
         } else {
           const float c2 = cm * kLog2e, m2 = msub * kLog2e;
 #pragma unroll
-          for (int e = 0; e < 32; ++e) xs[e] = exp2_fast(__builtin_fmaf(x[e], c2, -m2));
+          for (int e = 0; e < 32; ++e) x[e] = exp2_fast(__builtin_fmaf(x[e], c2, -m2));
         }
       }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) pk[i] = pack16x2<BF16>(xs[2 * i], xs[2 * i + 1]);
+      for (int i = 0; i < 16; ++i) pk[i] = pack16x2<BF16>(x[2 * i], x[2 * i + 1]);
     };
     auto psum = [&]() {
       // the normaliser sums exactly the rounded weights that feed P V
@@ -497,42 +499,38 @@ void attn_fwd_kernel(const AttnArgs a) {
       }
       return ps0 + ps1;
     };
+    // New reference maximum, chosen before the weights (a select, no
+    // branch), so that max, weights, packing and the row sum stay in one
+    // basic block with the P V products issued before them; the rescale of
+    // O and l and the update of m_run follow in a rare branch.  LAZY moves
+    // the reference only when a row's max grows by more than 8 (so p <= 2^8
+    // in between); the exact modes track the running maximum.
+    bool move;
+    float m_new;
     if constexpr (LAZY) {
-      // the reference maximum only moves when a row's max grows by more
-      // than 8 (so p <= 2^8 in between).  The weights are computed for the
-      // current reference first, in the same basic block as the P V
-      // products issued before them (the empty asm keeps them from being
-      // sunk into the branch), and recomputed in the rare case it moves.
-      weights(m_run);
-      float l_add = psum();
-      asm volatile("" : "+v"(l_add));
-      interleave_pv_softmax();
-      if (wave_any(mx > m_run + 8.f)) {
-        __builtin_amdgcn_sched_barrier(0);
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = (m_new == kNegInf) ? 1.f : exp2_fast(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < SH::ND; ++db) O[db] *= alpha;
-        m_run = m_new;
-        weights(m_run);
-        l_add = psum();
-      }
-      l_run += l_add;
+      move = wave_any(mx > m_run + 8.f);
+      m_new = move ? fmaxf(m_run, mx) : m_run;
     } else {
-      // exact running maximum: the weights use it directly
-      const float m_new = fmaxf(m_run, mx);
-      weights(m_new);
-      const float alpha = (m_run == kNegInf) ? 0.f : exp2_fast((m_run - m_new) * kLog2e);
-      l_run = __builtin_fmaf(l_run, alpha, psum());
-      interleave_pv_softmax();
-      if (wave_any(m_new != m_run)) {
-        __builtin_amdgcn_sched_barrier(0);
+      m_new = fmaxf(m_run, mx);
+      move = wave_any(m_new != m_run);
+    }
+    weights(m_new);
+    float l_add = psum();
+    // the weights must precede the branch (otherwise it is hoisted above
+    // them, which splits them off the P V products)
+    asm volatile("" : "+v"(l_add));
+    interleave_pv_softmax();
+    if (move) {
+      __builtin_amdgcn_sched_barrier(0);
+      float alpha;
+      if constexpr (LAZY) alpha = (m_new == kNegInf) ? 1.f : exp2_fast(m_run - m_new);
+      else alpha = (m_run == kNegInf) ? 0.f : exp2_fast((m_run - m_new) * kLog2e);
+      l_run *= alpha;
 #pragma unroll
-        for (int db = 0; db < SH::ND; ++db) O[db] *= alpha;
-      }
+      for (int db = 0; db < SH::ND; ++db) O[db] *= alpha;
       m_run = m_new;
     }
+    l_run += l_add;
   };
 
   // ---- main loop over key tiles, ascending.  Step kt computes the logits
