@@ -16,7 +16,9 @@ describes the attention kernel alone against the mix-weighted MFMA roofline
 T_roof = 2d N8 / P8 + 2d (N16 + Nflag) / P16 + 2d Nvalid / P16 with MI355X's
 published dense peaks P8 = 5.0e15 (int8 / fp8) and P16 = 2.5e15 (bf16 /
 fp16); `cpu_baseline` times the CPU oracle on a bounded sample of the same
-workload.
+workload.  `roofline.sustained` repeats the roofline against the dense MFMA
+rates this GPU sustains under a full-chip matrix load (measured live by a
+probe kernel, with the shader clock they ran at).
 """
 import argparse
 import hashlib
@@ -101,6 +103,53 @@ def algorithmic_flops(c, D):
 def roofline_time(c, D):
     return 2.0 * D * c["n8"] / PEAK8 + 2.0 * D * (c["n16"] + c["nflag"]) / PEAK16 + \
         2.0 * D * c["nvalid"] / PEAK16
+
+
+def roofline_time_at(c, D, p8, p16):
+    return 2.0 * D * c["n8"] / p8 + 2.0 * D * (c["n16"] + c["nflag"]) / p16 + \
+        2.0 * D * c["nvalid"] / p16
+
+
+# ---------------------------------------------------------------------------
+# sustained MFMA rates of this GPU (the published peaks assume the top engine
+# clock, which a full-chip matrix load does not hold)
+# ---------------------------------------------------------------------------
+
+def sustained_mfma_peaks(torch, iters=100000, reps=3):
+    """Dense bf16 and int8 MFMA rates with every SIMD's matrix pipe busy on
+    pseudo-random operands, and the shader clock meanwhile, from the probe
+    library built beside liblamp.so.  The int8 rate also stands for fp8 (the
+    same published dense rate).  None if the probe library is missing."""
+    import ctypes
+    path = os.path.join(ROOT, "mixed_precision_tiled_amd", "libmfma_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.mfma_probe_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint32,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.mfma_probe_launch.restype = ctypes.c_int
+    dev = torch.device("cuda:0")
+    nblk = 2 * torch.cuda.get_device_properties(0).multi_processor_count  # 2 waves per SIMD
+    sink = torch.empty(nblk * 256, dtype=torch.float32, device=dev)
+    clk = torch.zeros(2 * nblk, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {}
+    for kind, name, per_mfma in ((0, "bf16_fp16", 32768.0), (1, "int8_fp8", 65536.0)):
+        for r in range(reps):          # the last repetition is reported
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            rc = lib.mfma_probe_launch(kind, nblk, iters, 12345 + r, sink.data_ptr(),
+                                       clk.data_ptr(), stream)
+            e1.record()
+            torch.cuda.synchronize()
+            if rc != 0:
+                raise RuntimeError(f"mfma probe launch failed ({rc})")
+        t = e0.elapsed_time(e1) * 1e-3
+        ticks = clk.cpu().numpy().reshape(-1, 2).astype(np.float64)
+        out[name] = {"ops_per_s": nblk * 4 * iters * 4 * per_mfma / t,
+                     "clock_ghz": round(float(ticks[:, 0].sum() / ticks[:, 1].sum() * 0.1), 3)}
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -321,6 +370,16 @@ def main():
                      "peaks": {"int8_fp8": PEAK8, "bf16_fp16": PEAK16},
                      "kernel_source_sha256": kernel_source_hash()},
     }
+    sus = sustained_mfma_peaks(torch)
+    if sus is not None:
+        p8s, p16s = sus["int8_fp8"]["ops_per_s"], sus["bf16_fp16"]["ops_per_s"]
+        t_sus = roofline_time_at(c, cfg.D, p8s, p16s)
+        result["roofline"]["sustained"] = {
+            "peaks": {"int8_fp8": round(p8s, -9), "bf16_fp16": round(p16s, -9)},
+            "clock_ghz": {"int8_fp8": sus["int8_fp8"]["clock_ghz"],
+                          "bf16_fp16": sus["bf16_fp16"]["clock_ghz"]},
+            "t_roof_ms": round(t_sus * 1e3, 4), "frac": round(t_sus / attn_mean, 4)}
+        log(f"[bench] sustained MFMA: {json.dumps(result['roofline']['sustained'])}")
     if args.config == "C5" and not args.no_sweep:
         sweep = {}
         for code in ("i8", "e4m3"):

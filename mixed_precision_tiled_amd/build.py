@@ -1,7 +1,9 @@
 """Build liblamp.so (gfx950 only) in-tree with hipcc.
 
 Each translation unit is compiled to an object file in parallel, then linked
-into ``mixed_precision_tiled_amd/liblamp.so``.  Always rebuilds.
+into ``mixed_precision_tiled_amd/liblamp.so``.  The sustained-MFMA probe of
+the measurement harness is linked on its own into
+``mixed_precision_tiled_amd/libmfma_probe.so``.  Always rebuilds.
 """
 import os
 import subprocess
@@ -11,6 +13,8 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "liblamp.so")
+PROBE_SRC = os.path.join(HERE, "probe", "mfma_sustained.hip")
+PROBE_OUT = os.path.join(HERE, "libmfma_probe.so")
 BUILD = os.path.join(HERE, "_build")
 
 SOURCES = ["lamp_api.cpp", "quant_mask.hip", "attn_d64.hip", "attn_d128.hip", "attn_d256.hip"]
@@ -40,8 +44,15 @@ def build(verbose=False, jobs=None):
         _run([HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
         return obj
 
+    def compile_probe():
+        tmp = PROBE_OUT + ".tmp"
+        _run([HIPCC, *FLAGS, "-shared", PROBE_SRC, "-o", tmp])
+        os.replace(tmp, PROBE_OUT)
+
     with ThreadPoolExecutor(jobs) as ex:
+        probe = ex.submit(compile_probe)
         objs = list(ex.map(compile_one, SOURCES))
+        probe.result()
     tmp = OUT + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, OUT)

@@ -213,3 +213,21 @@ def test_bench_route_counts_match_oracle():
     # tile 0: 32 x 64 valid; tile 1 (keys 64..127): row r sees r - 63 keys;
     # tile 2 (keys 128..191): nothing valid for rows below 128
     assert c["nflag"] == 32 * 64 + sum(r - 63 for r in range(96, 128)) + 0
+
+
+def test_mfma_probe_library_loads():
+    """The measurement harness's sustained-MFMA probe is built beside the
+    library and exports its launcher; bad arguments are refused before any
+    launch."""
+    path = os.path.join(ROOT, "mixed_precision_tiled_amd", "libmfma_probe.so")
+    if not os.path.exists(path):
+        from mixed_precision_tiled_amd import build
+        build.build()
+    lib = ctypes.CDLL(path)
+    f = lib.mfma_probe_launch
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint32,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    assert f(2, 1, 1, 0, 16, 16, None) == -1     # unknown kind
+    assert f(0, 0, 1, 0, 16, 16, None) == -1     # no workgroups
+    assert f(0, 1, 1, 0, None, 16, None) == -1   # no sink
