@@ -15,6 +15,17 @@ Readings (listed in the design notes):
   ``seed``; with T = floor(f16 * 2**32) the group is 16-bit iff
   (r >> 32) < T, and its bit is 1 (8-bit) otherwise.
 
+Structured static template (the pages' routing policy is "static, data-free
+structured templates", TileMix section 4, with a "SpTrans75" configuration
+named in section 3 but not defined; the reading taken, after the fixed
+patterns of sparse transformers, is listed in the design notes): with the
+query tile's own group gq = min(n_g - 1, ((qt + 1)*tile_m - 1) // (G*tile_n))
+(the group of its last row's position) and d = |gq - g|, group g is 16-bit iff
+
+    g < sink   or   d < band   or   (stride > 0 and d % stride == 0),
+
+the same for every (b, h).
+
 SplitMix64 is the generator of Steele, Lea and Flood, "Fast Splittable
 Pseudorandom Number Generators" (OOPSLA 2014): the state advances by the
 golden-ratio increment 0x9E3779B97F4A7C15 and each output is the state passed
@@ -91,4 +102,30 @@ def build_mask(B, Hq, S_q, S_k, tile_m, tile_n, tiles_per_bit, frac_16bit, seed,
                words_per_row):
     """Packed mask words [B, Hq, n_qt, words_per_row] (uint64)."""
     bits = group_bits(B, Hq, S_q, S_k, tile_m, tile_n, tiles_per_bit, frac_16bit, seed)
+    return pack_bits(bits, words_per_row)
+
+
+def template_group_bits(B, Hq, S_q, S_k, tile_m, tile_n, tiles_per_bit, sink, band, stride):
+    """bits[b, h, qt, g] (uint8, 1 = 8-bit path) of the structured template:
+    the attention-sink groups, a local band around the query tile's own group
+    and every stride-th group from it are 16-bit, everything else 8-bit."""
+    if sink < 0 or band < 0 or stride < 0:
+        raise ValueError("template parameters must be >= 0")
+    n_qt = n_tiles(S_q, tile_m)
+    n_kt = n_tiles(S_k, tile_n)
+    n_g = n_tiles(n_kt, tiles_per_bit)
+    bits = np.ones((n_qt, n_g), dtype=np.uint8)
+    for qt in range(n_qt):
+        gq = min(n_g - 1, ((qt + 1) * tile_m - 1) // (tiles_per_bit * tile_n))
+        for g in range(n_g):
+            d = abs(gq - g)
+            if g < sink or d < band or (stride > 0 and d % stride == 0):
+                bits[qt, g] = 0
+    return np.broadcast_to(bits, (B, Hq, n_qt, n_g)).copy()
+
+
+def build_mask_template(B, Hq, S_q, S_k, tile_m, tile_n, tiles_per_bit, sink, band, stride,
+                        words_per_row):
+    """Packed words [B, Hq, n_qt, words_per_row] (uint64) of the structured template."""
+    bits = template_group_bits(B, Hq, S_q, S_k, tile_m, tile_n, tiles_per_bit, sink, band, stride)
     return pack_bits(bits, words_per_row)

@@ -86,3 +86,72 @@ def test_pack_unpack_roundtrip():
     assert (mask.unpack_bits(mask.pack_bits(bits, 3), 130) == bits).all()
     with pytest.raises(ValueError):
         mask.pack_bits(bits, 2)
+
+
+# ---------------------------------------------------------------------------
+# structured static template: expected bit rows written out by hand from the
+# definition (g < sink, or d < band, or d % stride == 0 with d = |gq - g|)
+# ---------------------------------------------------------------------------
+
+def _rows(strings):
+    return np.array([[int(c) for c in r] for r in strings], dtype=np.uint8)
+
+
+def test_template_hand_worked_square():
+    # tile_m = tile_n = 64, G = 1, S = 512: 8 query tiles, 8 groups, gq = qt;
+    # sink 1, band 2, stride 3.  Row qt lists bits g = 0..7 (0 = 16-bit).
+    want = _rows(["00101101",    # qt 0: 16-bit {0, 1, 3, 6}
+                  "00010110",    # qt 1: {0, 1, 2, 4, 7}
+                  "00001011",    # qt 2: {0, 1, 2, 3, 5}
+                  "01000101",    # qt 3: {0, 2, 3, 4, 6}
+                  "00100010",    # qt 4: {0, 1, 3, 4, 5, 7}
+                  "01010001",    # qt 5: {0, 2, 4, 5, 6}
+                  "01101000",    # qt 6: {0, 3, 5, 6, 7}
+                  "00110100"])   # qt 7: {0, 1, 4, 6, 7}
+    got = mask.template_group_bits(1, 1, 512, 512, 64, 64, 1, 1, 2, 3)[0, 0]
+    assert (got == want).all()
+
+
+def test_template_hand_worked_tall_tiles():
+    # tile_m = 128, tile_n = 64, G = 1, S = 512: gq = 2 qt + 1 (the group of
+    # the tile's last row); band 3 only
+    want = _rows(["00001111",    # gq 1: groups 0..3
+                  "10000011",    # gq 3: groups 1..5
+                  "11100000",    # gq 5: groups 3..7
+                  "11111000"])   # gq 7: groups 5..7
+    got = mask.template_group_bits(2, 3, 512, 512, 128, 64, 1, 0, 3, 0)
+    assert got.shape == (2, 3, 4, 8)
+    for b in range(2):
+        for h in range(3):
+            assert (got[b, h] == want).all()
+
+
+def test_template_extremes_and_grouping():
+    # no template part: everything 8-bit; a band covering every group or a
+    # sink of n_g groups: everything 16-bit; stride 1: everything 16-bit
+    assert mask.template_group_bits(1, 2, 1000, 1000, 128, 64, 4, 0, 0, 0).all()
+    n_g = -(-(-(-1000 // 64)) // 4)
+    for sink, band, stride in ((n_g, 0, 0), (0, n_g, 0), (0, 0, 1)):
+        assert not mask.template_group_bits(1, 2, 1000, 1000, 128, 64, 4, sink, band, stride).any()
+    # G = 4 groups of 256 keys, tile_m = 128: query tiles 2j and 2j+1 share gq = j
+    bits = mask.template_group_bits(1, 1, 2048, 2048, 128, 64, 4, 0, 1, 0)[0, 0]
+    for qt in range(16):
+        assert bits[qt].tolist() == [0 if g == qt // 2 else 1 for g in range(8)]
+    # keys beyond the queries (S_k > S_q, non-causal use): gq clamps below n_g
+    bits = mask.template_group_bits(1, 1, 128, 1024, 128, 64, 1, 0, 1, 0)[0, 0]
+    assert bits.tolist() == [[1, 0] + [1] * 14]
+    # queries beyond the keys: gq clamps to the last group
+    bits = mask.template_group_bits(1, 1, 1024, 128, 128, 64, 1, 0, 1, 0)[0, 0]
+    assert (bits[:, 1] == 0).all() and (bits[:, 0] == 1).all()
+
+
+def test_template_packing_multiword():
+    # 200 groups need 4 words; bit g sits in word g // 64 at g % 64
+    B, Hq, S, tm, tn, G = 1, 1, 200 * 64, 128, 64, 1
+    bits = mask.template_group_bits(B, Hq, S, S, tm, tn, G, 3, 4, 17)
+    words = mask.build_mask_template(B, Hq, S, S, tm, tn, G, 3, 4, 17, 5)
+    assert words.shape == (1, 1, 100, 5) and (words[..., 4] == 0).all()
+    for qt in (0, 37, 99):
+        for g in range(200):
+            w, bit = divmod(g, 64)
+            assert ((int(words[0, 0, qt, w]) >> bit) & 1) == bits[0, 0, qt, g]
