@@ -222,8 +222,9 @@ def cpu_baseline(cfg, q, k, v, budget_s=12.0):
 class Pipeline:
     """Preallocated buffers for one configuration; run() enqueues one step."""
 
-    def __init__(self, L, cfg, qd, kd, vd, torch):
+    def __init__(self, L, cfg, qd, kd, vd, torch, template=None):
         self.L, self.cfg, self.torch = L, cfg, torch
+        self.template = template       # (sink, band, stride) groups, or the random mask
         self.qd, self.kd, self.vd = qd, kd, vd
         dev = qd.device
         B, Hq, Hkv, S, D = cfg.B, cfg.Hq, cfg.Hkv, cfg.S, cfg.D
@@ -242,8 +243,12 @@ class Pipeline:
         L, c = self.L, self.cfg
         L.lamp_quantize_blocks(self.qd, c.tile_m, c.code, codes=self.q8, scales=self.sq)
         L.lamp_quantize_blocks(self.kd, c.tile_n, c.code, codes=self.k8, scales=self.sk)
-        L.lamp_build_mask(c.B, c.Hq, c.S, c.S, c.tile_m, c.tile_n, c.tiles_per_bit, self.f16,
-                          c.mask_seed, c.words_per_row, mask=self.mask)
+        if self.template is not None:
+            L.lamp_build_mask_template(c.B, c.Hq, c.S, c.S, c.tile_m, c.tile_n, c.tiles_per_bit,
+                                       *self.template, c.words_per_row, mask=self.mask)
+        else:
+            L.lamp_build_mask(c.B, c.Hq, c.S, c.S, c.tile_m, c.tile_n, c.tiles_per_bit, self.f16,
+                              c.mask_seed, c.words_per_row, mask=self.mask)
 
     def attn(self):
         L, c = self.L, self.cfg
@@ -396,6 +401,22 @@ def main():
                     "roofline_frac": round(tr / float(np.median(ts)), 4),
                     "t_roof_ms": round(tr * 1e3, 4)}
                 del sp
+        # a structured static template with about a quarter of the valid
+        # elements on the 16-bit path (sink group, band of 2, every 5th group)
+        tpl = (1, 2, 5)
+        sc = get_config("C5", 0.25, "i8")
+        sp = Pipeline(L, sc, qd, kd, vd, torch, template=tpl)
+        sp.prep()
+        ts = time_attn(torch, sp, iters=5, warmup=1)
+        cc = sp.counts()
+        tr = roofline_time(cc, sc.D)
+        sweep["i8_template_sink1_band2_stride5"] = {
+            "attn_ms": round(float(np.median(ts)) * 1e3, 4),
+            "tflops": round(algorithmic_flops(cc, sc.D) / float(np.median(ts)) / 1e12, 1),
+            "roofline_frac": round(tr / float(np.median(ts)), 4),
+            "t_roof_ms": round(tr * 1e3, 4),
+            "frac_16bit_elements": round(cc["n16"] / cc["nvalid"], 4)}
+        del sp
         result["sweep_c5_attention"] = sweep
         log(f"[bench] sweep {json.dumps(sweep)}")
     if not args.no_cpu:

@@ -114,6 +114,32 @@ lamp_status lamp_build_mask(int64_t B, int64_t Hq, int64_t S_q, int64_t S_k, int
                             void* stream);
 
 /*
+ * lamp_build_mask_template -- a structured static packed precision mask.
+ *
+ * Source: TileMix page, section 4 "Why It Matters" (the routing policy is
+ * static, data-free structured templates) and section 3 (a "SpTrans75"
+ * configuration, named but not defined).  Reading taken: the fixed local and
+ * strided patterns of sparse transformers plus attention-sink groups, at
+ * group granularity.  Layout, group definition and bit polarity as for
+ * lamp_build_mask.  For query tile qt let
+ *   gq = min(n_g - 1, ((qt + 1) * tile_m - 1) / (tiles_per_bit * tile_n))
+ * (the group holding the tile's last row position) and d = |gq - g|; group g
+ * is 16-bit (bit 0) iff
+ *   g < sink_groups, or d < band_groups, or (stride_groups > 0 and
+ *   d % stride_groups == 0),
+ * and 8-bit (bit 1) otherwise; every (b, h) gets the same rows.
+ * sink_groups, band_groups, stride_groups >= 0 (LAMP_ERR_SHAPE otherwise).
+ *
+ * mask    [B, Hq, ceil(S_q / tile_m), words_per_row] uint64, 8-byte aligned;
+ *         words_per_row >= ceil(n_g / 64).
+ */
+lamp_status lamp_build_mask_template(int64_t B, int64_t Hq, int64_t S_q, int64_t S_k,
+                                     int32_t tile_m, int32_t tile_n, int32_t tiles_per_bit,
+                                     int32_t sink_groups, int32_t band_groups,
+                                     int32_t stride_groups, uint64_t* mask,
+                                     int32_t words_per_row, void* stream);
+
+/*
  * lamp_attn_fwd -- the dual-path fused attention forward.
  *
  * Sources: TileMix page, section 2 (tile loop, per-group dispatch, shared

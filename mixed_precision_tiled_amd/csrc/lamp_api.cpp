@@ -130,6 +130,43 @@ lamp_status lamp_build_mask(int64_t B, int64_t Hq, int64_t S_q, int64_t S_k, int
   return hip_status(lamp::launch_build_mask(a, static_cast<hipStream_t>(stream)), "mask launch");
 }
 
+lamp_status lamp_build_mask_template(int64_t B, int64_t Hq, int64_t S_q, int64_t S_k,
+                                     int32_t tile_m, int32_t tile_n, int32_t tiles_per_bit,
+                                     int32_t sink_groups, int32_t band_groups,
+                                     int32_t stride_groups, uint64_t* mask,
+                                     int32_t words_per_row, void* stream) {
+  if (B < 0 || Hq < 0 || S_q < 0 || S_k < 0) return fail(LAMP_ERR_SHAPE, "negative size");
+  if (tile_m <= 0 || tile_n <= 0 || tiles_per_bit <= 0)
+    return fail(LAMP_ERR_SHAPE, "tile sizes and tiles_per_bit must be positive");
+  if (sink_groups < 0 || band_groups < 0 || stride_groups < 0)
+    return fail(LAMP_ERR_SHAPE, "template parameters must be >= 0");
+  if ((int64_t)tiles_per_bit * tile_n > INT32_MAX)
+    return fail(LAMP_ERR_UNSUPPORTED, "tiles_per_bit * tile_n too large");
+  if (S_q > kMaxSeq || S_k > kMaxSeq) return fail(LAMP_ERR_UNSUPPORTED, "sequence too long");
+  const int64_t n_qt = cdiv(S_q, tile_m), n_kt = cdiv(S_k, tile_n);
+  const int64_t n_g = cdiv(n_kt, tiles_per_bit);
+  if (words_per_row < cdiv(n_g, 64) || words_per_row < 1)
+    return fail(LAMP_ERR_UNSUPPORTED, "words_per_row=%d < ceil(n_g/64)=%lld", words_per_row,
+                (long long)cdiv(n_g, 64));
+  if (B == 0 || Hq == 0 || S_q == 0) return ok();
+  if (!mask) return fail(LAMP_ERR_NULL, "mask is required");
+  if (reinterpret_cast<uintptr_t>(mask) & 7u) return fail(LAMP_ERR_ALIGN, "mask needs 8-byte alignment");
+  lamp::TemplateMaskArgs a{};
+  a.mask = mask;
+  a.total_words = B * Hq * n_qt * words_per_row;
+  if (cdiv(a.total_words, 256) > kMaxGrid) return fail(LAMP_ERR_UNSUPPORTED, "mask too large");
+  a.words_per_row = words_per_row;
+  a.n_g = (int32_t)n_g;
+  a.n_qt = (int32_t)n_qt;
+  a.tile_m = tile_m;
+  a.group_keys = tiles_per_bit * tile_n;
+  a.sink = sink_groups;
+  a.band = band_groups;
+  a.stride = stride_groups;
+  return hip_status(lamp::launch_build_mask_template(a, static_cast<hipStream_t>(stream)),
+                    "template mask launch");
+}
+
 lamp_status lamp_attn_fwd(const lamp_attn_params* p, void* stream) {
   if (!p) return fail(LAMP_ERR_NULL, "params is NULL");
   if (p->struct_size != sizeof(lamp_attn_params))

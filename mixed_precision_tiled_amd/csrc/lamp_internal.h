@@ -27,6 +27,17 @@ struct MaskArgs {
   int32_t n_g;
 };
 
+struct TemplateMaskArgs {
+  uint64_t* mask;
+  int64_t total_words;         // B * Hq * n_qt * words_per_row
+  int32_t words_per_row;
+  int32_t n_g;
+  int32_t n_qt;
+  int32_t tile_m;
+  int32_t group_keys;          // tiles_per_bit * tile_n
+  int32_t sink, band, stride;
+};
+
 struct AttnArgs {
   const void* q;
   const void* k;
@@ -64,6 +75,7 @@ struct AttnConfig {
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
 hipError_t launch_build_mask(const MaskArgs& a, hipStream_t s);
+hipError_t launch_build_mask_template(const TemplateMaskArgs& a, hipStream_t s);
 hipError_t launch_attn_d64(const AttnArgs& a, const AttnConfig& c, hipStream_t s);
 hipError_t launch_attn_d128(const AttnArgs& a, const AttnConfig& c, hipStream_t s);
 hipError_t launch_attn_d256(const AttnArgs& a, const AttnConfig& c, hipStream_t s);

@@ -134,6 +134,27 @@ __global__ __launch_bounds__(256) void build_mask_kernel(MaskArgs a) {
   a.mask[wid] = word;
 }
 
+// Structured template: one thread per mask word; the rule depends only on
+// the query tile and the group.
+__global__ __launch_bounds__(256) void build_mask_template_kernel(TemplateMaskArgs a) {
+  const int64_t wid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (wid >= a.total_words) return;
+  const int64_t row = wid / a.words_per_row;        // (b*Hq + h)*n_qt + qt
+  const int w = (int)(wid % a.words_per_row);
+  const int qt = (int)(row % a.n_qt);
+  const int gq = (int)min((int64_t)a.n_g - 1, ((int64_t)(qt + 1) * a.tile_m - 1) / a.group_keys);
+  uint64_t word = 0;
+  const int g0 = w * 64;
+  const int gn = min(64, a.n_g - g0);
+  for (int i = 0; i < gn; ++i) {
+    const int g = g0 + i;
+    const int d = gq >= g ? gq - g : g - gq;
+    const bool is16 = g < a.sink || d < a.band || (a.stride > 0 && d % a.stride == 0);
+    word |= (uint64_t)(!is16) << i;
+  }
+  a.mask[wid] = word;
+}
+
 }  // namespace
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
@@ -149,6 +170,12 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
 hipError_t launch_build_mask(const MaskArgs& a, hipStream_t s) {
   const unsigned blocks = (unsigned)((a.total_words + 255) / 256);
   hipLaunchKernelGGL(build_mask_kernel, dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_build_mask_template(const TemplateMaskArgs& a, hipStream_t s) {
+  const unsigned blocks = (unsigned)((a.total_words + 255) / 256);
+  hipLaunchKernelGGL(build_mask_template_kernel, dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

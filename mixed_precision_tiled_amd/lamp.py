@@ -61,6 +61,9 @@ _lib.lamp_build_mask.restype = _i32
 _lib.lamp_build_mask.argtypes = [_i64, _i64, _i64, _i64, _i32, _i32, _i32, ctypes.c_double, _u64,
                                  _vp, _i32, _vp]
 _lib.lamp_attn_fwd.restype = _i32
+_lib.lamp_build_mask_template.restype = _i32
+_lib.lamp_build_mask_template.argtypes = [_i64, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _i32,
+                                          _i32, _vp, _i32, _vp]
 _lib.lamp_attn_fwd.argtypes = [ctypes.POINTER(lamp_attn_params), _vp]
 _lib.lamp_status_string.restype = ctypes.c_char_p
 _lib.lamp_status_string.argtypes = [_i32]
@@ -154,6 +157,24 @@ def lamp_build_mask(B, Hq, S_q, S_k, tile_m, tile_n, tiles_per_bit, frac_16bit, 
         raise ValueError("mask must be contiguous")
     _check(_lib.lamp_build_mask(B, Hq, S_q, S_k, tile_m, tile_n, tiles_per_bit, float(frac_16bit),
                                 seed & ((1 << 64) - 1), _ptr(mask), W, _stream(mask)))
+    return mask
+
+
+def lamp_build_mask_template(B, Hq, S_q, S_k, tile_m, tile_n, tiles_per_bit, sink_groups,
+                             band_groups, stride_groups, words_per_row=None, mask=None,
+                             device="cuda"):
+    """Structured static packed mask (sink groups, local band, strided
+    groups), int64 tensor [B, Hq, n_qt, W] holding the uint64 words."""
+    n_qt = cdiv(S_q, tile_m)
+    n_g = cdiv(cdiv(S_k, tile_n), tiles_per_bit)
+    W = words_per_row or max(1, cdiv(n_g, 64))
+    if mask is None:
+        mask = torch.empty((B, Hq, n_qt, W), dtype=torch.int64, device=device)
+    if not mask.is_contiguous():
+        raise ValueError("mask must be contiguous")
+    _check(_lib.lamp_build_mask_template(B, Hq, S_q, S_k, tile_m, tile_n, tiles_per_bit,
+                                         sink_groups, band_groups, stride_groups, _ptr(mask), W,
+                                         _stream(mask)))
     return mask
 
 

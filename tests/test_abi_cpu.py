@@ -14,11 +14,20 @@ HEADER = os.path.join(ROOT, "include", "lamp.h")
 LIB = os.path.join(ROOT, "mixed_precision_tiled_amd", "liblamp.so")
 
 
+def build_module():
+    """build.py loaded by path (importing the package needs a built library)."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_lamp_build", os.path.join(ROOT, "mixed_precision_tiled_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
 @pytest.fixture(scope="session")
 def lamp():
     if not os.path.exists(LIB):
-        from mixed_precision_tiled_amd import build
-        build.build()
+        build_module().build()
     import mixed_precision_tiled_amd as m
     return m
 
@@ -120,6 +129,24 @@ def test_mask_validation(lamp):
     assert f(0, 1, 256, 256, 64, 64, 1, 0.5, 0, None, 1, None) == 0
 
 
+def test_mask_template_validation(lamp):
+    f = _lib(lamp).lamp_build_mask_template
+    p = ctypes.c_void_p(64)
+    # negative template parameters
+    assert f(1, 1, 256, 256, 64, 64, 1, -1, 2, 0, p, 1, None) == 2
+    assert f(1, 1, 256, 256, 64, 64, 1, 1, -2, 0, p, 1, None) == 2
+    assert f(1, 1, 256, 256, 64, 64, 1, 1, 2, -3, p, 1, None) == 2
+    # tiles
+    assert f(1, 1, 256, 256, 0, 64, 1, 1, 2, 0, p, 1, None) == 2
+    assert f(1, 1, 256, 256, 64, 64, 0, 1, 2, 0, p, 1, None) == 2
+    assert f(1, 1, 256, 256, 64, 1 << 20, 1 << 12, 1, 2, 0, p, 1, None) == 3
+    # words, pointers, alignment, empty problem
+    assert f(1, 1, 8192, 8192, 128, 64, 1, 1, 2, 0, p, 1, None) == 3
+    assert f(1, 1, 256, 256, 64, 64, 1, 1, 2, 0, None, 1, None) == 1
+    assert f(1, 1, 256, 256, 64, 64, 1, 1, 2, 0, ctypes.c_void_p(65), 1, None) == 4
+    assert f(0, 1, 256, 256, 64, 64, 1, 1, 2, 0, None, 1, None) == 0
+
+
 def _params(lamp, **kw):
     from mixed_precision_tiled_amd.lamp import lamp_attn_params as P
     p = P()
@@ -183,7 +210,7 @@ def test_attn_validation_strides(lamp):
 
 
 def test_build_flags():
-    from mixed_precision_tiled_amd import build
+    build = build_module()
     assert "--offload-arch=gfx950" in build.FLAGS
     i = build.FLAGS.index("-target-feature")
     assert build.FLAGS[i - 1] == "-Xclang" and build.FLAGS[i + 1:i + 3] == ["-Xclang", "-packed-fp32-ops"]
@@ -221,8 +248,7 @@ def test_mfma_probe_library_loads():
     launch."""
     path = os.path.join(ROOT, "mixed_precision_tiled_amd", "libmfma_probe.so")
     if not os.path.exists(path):
-        from mixed_precision_tiled_amd import build
-        build.build()
+        build_module().build()
     lib = ctypes.CDLL(path)
     f = lib.mfma_probe_launch
     f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint32,

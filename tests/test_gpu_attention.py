@@ -305,3 +305,37 @@ def test_error_paths():
         lamp.lamp_attn_fwd(qd, kd, vd, q8, k8, sq, sk, mk, code="i8", causal=True, tile_m=96,
                            tiles_per_bit=1)
     assert e.value.status == lamp.lamp.LAMP_ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------------------
+# structured static template masks: the GPU-built template drives the kernel
+# ---------------------------------------------------------------------------
+
+TEMPLATE = [
+    # D, tm, dtype, code, causal, Hq, Hkv, S, G, sink, band, stride
+    (128, 128, "bf16", "i8", True, 4, 2, 1000, 1, 1, 2, 4),
+    (64, 64, "f16", "e4m3", True, 2, 1, 700, 2, 0, 1, 3),
+    (128, 128, "bf16", "i8", False, 2, 2, 520, 1, 2, 1, 0),
+]
+
+
+@pytest.mark.parametrize("case", TEMPLATE, ids=lambda c: "d{}_m{}_{}_{}_{}_s{}_t{}.{}.{}".format(
+    c[0], c[1], c[2], c[3], "causal" if c[4] else "full", c[7], c[9], c[10], c[11]))
+def test_template_tilemix(case):
+    import mixed_precision_tiled_amd as L
+    D, tm, dt, code, causal, Hq, Hkv, S, G, sink, band, stride = case
+    cfg = small_cfg(D, tm, dt, code, causal, 1, Hq, Hkv, S, G, 0.5)
+    q, k, v = inputs_qk(cfg, S, S)
+    print(f"[attn] template {case}", flush=True)
+    n_g = -(-(-(-S // cfg.tile_n)) // G)
+    W = max(1, -(-n_g // 64))
+    m = L.lamp_build_mask_template(1, Hq, S, S, tm, cfg.tile_n, G, sink, band, stride, W,
+                                   device=device())
+    words = m.cpu().numpy().view(np.uint64)
+    ref = omask.build_mask_template(1, Hq, S, S, tm, cfg.tile_n, G, sink, band, stride, W)
+    assert (words == ref).all()
+    g = gpu_run(cfg, q, k, v, mask_words=words)
+    P = oracle_problem(cfg, q, k, v, mask_words=ref)
+    check_codes_and_mask(cfg, P, g)
+    for h in range(Hq):
+        check_head(cfg, P, g, 0, h)

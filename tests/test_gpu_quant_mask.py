@@ -153,3 +153,24 @@ def test_mask_bit_exact(shape):
         torch.cuda.synchronize()
         ref = omask.build_mask(B, Hq, S_q, S_k, tm, tn, G, f16, seed, w)
         assert (m.cpu().numpy().view(np.uint64) == ref).all()
+
+
+@pytest.mark.parametrize("shape", [
+    (1, 1, 512, 512, 64, 64, 1, 1, 2, 3),
+    (2, 32, 16384, 16384, 128, 64, 4, 1, 2, 8),
+    (1, 4, 8192, 8192, 128, 64, 1, 2, 3, 16),      # 128 groups: two words
+    (3, 5, 1000, 777, 64, 64, 3, 0, 1, 0),
+    (1, 2, 4096, 70000, 128, 64, 1, 4, 5, 33),     # keys beyond the queries
+    (1, 1, 70000, 4096, 128, 64, 2, 0, 3, 5),      # queries beyond the keys
+    (1, 3, 2048, 2048, 128, 64, 4, 0, 0, 0),       # no template part: all 8-bit
+])
+def test_mask_template_bit_exact(shape):
+    B, Hq, S_q, S_k, tm, tn, G, sink, band, stride = shape
+    n_g = -(-(-(-S_k // tn)) // G)
+    W = max(1, -(-n_g // 64))
+    for w in (W, W + 1):
+        m = L().lamp_build_mask_template(B, Hq, S_q, S_k, tm, tn, G, sink, band, stride, w,
+                                         device=dev())
+        torch.cuda.synchronize()
+        ref = omask.build_mask_template(B, Hq, S_q, S_k, tm, tn, G, sink, band, stride, w)
+        assert (m.cpu().numpy().view(np.uint64) == ref).all()
