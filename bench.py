@@ -69,10 +69,11 @@ def tile_valid_counts(S_q, S_k, tile_m, tile_n, causal):
     if not causal:
         return np.outer(r1 - r0, c1 - c0).astype(np.int64)
     cnt = np.zeros((n_qt, n_kt), dtype=np.int64)
+    off = S_k - S_q                   # causal: query i sees keys j <= i + off
     for a in range(n_qt):
         rows = np.arange(r0[a], r1[a])
-        # valid keys per row within the tile: clip(row + 1, c0, c1) - c0
-        cnt[a] = (np.clip(rows[:, None] + 1, c0[None, :], c1[None, :]) - c0[None, :]).sum(0)
+        # valid keys per row within the tile: clip(row + off + 1, c0, c1) - c0
+        cnt[a] = (np.clip(rows[:, None] + off + 1, c0[None, :], c1[None, :]) - c0[None, :]).sum(0)
     return cnt
 
 

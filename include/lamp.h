@@ -122,9 +122,10 @@ lamp_status lamp_build_mask(int64_t B, int64_t Hq, int64_t S_q, int64_t S_k, int
  * strided patterns of sparse transformers plus attention-sink groups, at
  * group granularity.  Layout, group definition and bit polarity as for
  * lamp_build_mask.  For query tile qt let
- *   gq = min(n_g - 1, ((qt + 1) * tile_m - 1) / (tiles_per_bit * tile_n))
- * (the group holding the tile's last row position) and d = |gq - g|; group g
- * is 16-bit (bit 0) iff
+ *   pos = (qt + 1) * tile_m - 1 + S_k - S_q
+ * (the key position of the tile's last row, queries aligned with the end of
+ * the keys as for causal attention), gq = clamp(floor(pos / (tiles_per_bit *
+ * tile_n)), 0, n_g - 1) and d = |gq - g|; group g is 16-bit (bit 0) iff
  *   g < sink_groups, or d < band_groups, or (stride_groups > 0 and
  *   d % stride_groups == 0),
  * and 8-bit (bit 1) otherwise; every (b, h) gets the same rows.
@@ -147,7 +148,9 @@ lamp_status lamp_build_mask_template(int64_t B, int64_t Hq, int64_t S_q, int64_t
  * abstract (8-bit exponentials, adaptive sub-block recompute in 16 bits).
  *
  * For query row i of head h (KV head h / (Hq / Hkv)) and key j:
- *   valid(i, j)  = j < S_k, and j <= i when causal (then S_q == S_k);
+ *   valid(i, j)  = j < S_k, and j <= i + S_k - S_q when causal (then
+ *                  S_q <= S_k: the queries are the last S_q positions, as
+ *                  for a chunk of new tokens after S_k - S_q earlier ones);
  *   route8(i, j) = mask bit of (b, h, i / tile_m, (j / tile_n) / G);
  *   s16 = sm * q_i . k_j            s8 = (cq_i . ck_j) * sQ * sK * sm.
  * MODE_MASK, exp8 = 0: O_i = softmax over valid j of the routed logits, times V.

@@ -122,13 +122,15 @@ void attn_fwd_kernel(const AttnArgs a) {
   const bool wave_live = row0 < a.S_q;
   const int q_row = min(my_row, a.S_q - 1);
 
+  // causal: query row i sits at key position i + coff and sees keys up to it
+  const int coff = a.S_k - a.S_q;
   const int wg_last = min(a.S_q, (qt + 1) * SH::TM) - 1;
-  const int kt_end = a.causal ? min(a.n_kt, wg_last / 64 + 1) : a.n_kt;
+  const int kt_end = a.causal ? min(a.n_kt, (wg_last + coff) / 64 + 1) : a.n_kt;
   const int w_last = min(a.S_q, row0 + 32) - 1;
-  const int kt_end_w = !wave_live ? 0 : (a.causal ? min(a.n_kt, w_last / 64 + 1) : a.n_kt);
+  const int kt_end_w = !wave_live ? 0 : (a.causal ? min(a.n_kt, (w_last + coff) / 64 + 1) : a.n_kt);
   const bool rows_ragged = row0 + 32 > a.S_q;
   // largest valid key index of this lane's row (-1: row beyond S_q)
-  const int key_lim = my_row >= a.S_q ? -1 : (a.causal ? min(my_row, a.S_k - 1) : a.S_k - 1);
+  const int key_lim = my_row >= a.S_q ? -1 : (a.causal ? min(my_row + coff, a.S_k - 1) : a.S_k - 1);
 
   // ---- Q fragments (B operand of S^T = K Q^T), resident for the whole loop
   const char* qp = reinterpret_cast<const char*>(a.q) +
@@ -364,7 +366,7 @@ void attn_fwd_kernel(const AttnArgs a) {
   auto qk_part = [&](int kt, const char* kb, bool is8, float sK, float* x) -> Logits {
     const int key0 = kt * SH::TN;
     const bool need_mask = rows_ragged || (key0 + SH::TN > a.S_k) ||
-                           (a.causal && key0 + SH::TN - 1 > row0);
+                           (a.causal && key0 + SH::TN - 1 > row0 + coff);
     // valid(e) <=> kofs(e) <= lim_rel
     const int lim_rel = key_lim - key0 - 4 * hf;
     Logits lg;

@@ -160,6 +160,7 @@ lamp_status lamp_build_mask_template(int64_t B, int64_t Hq, int64_t S_q, int64_t
   a.n_qt = (int32_t)n_qt;
   a.tile_m = tile_m;
   a.group_keys = tiles_per_bit * tile_n;
+  a.pos_off = S_k - S_q;
   a.sink = sink_groups;
   a.band = band_groups;
   a.stride = stride_groups;
@@ -190,7 +191,7 @@ lamp_status lamp_attn_fwd(const lamp_attn_params* p, void* stream) {
     return fail(LAMP_ERR_UNSUPPORTED, "Hq=%lld must be a positive multiple of Hkv=%lld",
                 (long long)p->Hq, (long long)p->Hkv);
   if (p->causal != 0 && p->causal != 1) return fail(LAMP_ERR_SHAPE, "causal must be 0 or 1");
-  if (p->causal && p->S_q != p->S_k) return fail(LAMP_ERR_UNSUPPORTED, "causal needs S_q == S_k");
+  if (p->causal && p->S_q > p->S_k) return fail(LAMP_ERR_UNSUPPORTED, "causal needs S_q <= S_k");
   if (p->exp8 != 0 && p->exp8 != 1) return fail(LAMP_ERR_SHAPE, "exp8 must be 0 or 1");
   if (p->mode == LAMP_MODE_ADAPTIVE) {
     if (p->sub_rows != 32) return fail(LAMP_ERR_UNSUPPORTED, "sub_rows must be 32");

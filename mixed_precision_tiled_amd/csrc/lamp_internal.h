@@ -36,6 +36,7 @@ struct TemplateMaskArgs {
   int32_t tile_m;
   int32_t group_keys;          // tiles_per_bit * tile_n
   int32_t sink, band, stride;
+  int64_t pos_off;             // S_k - S_q: key position of query row 0
 };
 
 struct AttnArgs {

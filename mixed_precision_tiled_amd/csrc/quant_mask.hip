@@ -142,7 +142,10 @@ __global__ __launch_bounds__(256) void build_mask_template_kernel(TemplateMaskAr
   const int64_t row = wid / a.words_per_row;        // (b*Hq + h)*n_qt + qt
   const int w = (int)(wid % a.words_per_row);
   const int qt = (int)(row % a.n_qt);
-  const int gq = (int)min((int64_t)a.n_g - 1, ((int64_t)(qt + 1) * a.tile_m - 1) / a.group_keys);
+  // key position of the tile's last row (floor division: it may be negative)
+  const int64_t pos = (int64_t)(qt + 1) * a.tile_m - 1 + a.pos_off;
+  const int64_t gpos = pos >= 0 ? pos / a.group_keys : -((-pos + a.group_keys - 1) / a.group_keys);
+  const int gq = (int)min((int64_t)a.n_g - 1, max((int64_t)0, gpos));
   uint64_t word = 0;
   const int g0 = w * 64;
   const int gn = min(64, a.n_g - g0);

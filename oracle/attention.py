@@ -33,7 +33,10 @@ Logits (fp64):
             are summed)
 
 Readings where the pages are silent (listed in the design notes): causal
-means S_q == S_k and j <= i; GQA maps query head h to KV head
+aligns the queries with the end of the keys, as for a chunk of S_q new
+queries after S_k - S_q earlier tokens: query i sits at key position
+i + S_k - S_q and sees keys j <= i + S_k - S_q (so S_q <= S_k; S_q == S_k is
+the plain lower triangle); GQA maps query head h to KV head
 h // (Hq / Hkv); sm defaults to 1 / sqrt(D); the 8-bit logit that is rounded
 is the max-shifted x = s - m_new, then exp(x) is rounded again, both to E4M3
 with round-to-nearest-even and saturation; alpha = exp(m - m_new) is full
@@ -77,8 +80,8 @@ class Problem:
         _, Hkv, S_k, _ = self.k.shape
         if Hq % Hkv:
             raise ValueError("Hq must be a multiple of Hkv")
-        if self.causal and S_q != S_k:
-            raise ValueError("causal needs S_q == S_k")
+        if self.causal and S_q > S_k:
+            raise ValueError("causal needs S_q <= S_k")
         if self.sm_scale <= 0:
             self.sm_scale = 1.0 / np.sqrt(D)
         self.B, self.Hq, self.Hkv, self.S_q, self.S_k, self.D = B, Hq, Hkv, S_q, S_k, D
@@ -100,7 +103,7 @@ class Problem:
     def valid(self, rows, cols):
         ok = (cols[None, :] < self.S_k) & (rows[:, None] < self.S_q)
         if self.causal:
-            ok &= cols[None, :] <= rows[:, None]
+            ok &= cols[None, :] <= rows[:, None] + (self.S_k - self.S_q)
         return ok
 
 

@@ -19,8 +19,10 @@ Structured static template (the pages' routing policy is "static, data-free
 structured templates", TileMix section 4, with a "SpTrans75" configuration
 named in section 3 but not defined; the reading taken, after the fixed
 patterns of sparse transformers, is listed in the design notes): with the
-query tile's own group gq = min(n_g - 1, ((qt + 1)*tile_m - 1) // (G*tile_n))
-(the group of its last row's position) and d = |gq - g|, group g is 16-bit iff
+query tile's own group gq = clamp((pos) // (G*tile_n), 0, n_g - 1), pos =
+(qt + 1)*tile_m - 1 + S_k - S_q the key position of its last row (queries
+aligned with the end of the keys, as for causal attention), and
+d = |gq - g|, group g is 16-bit iff
 
     g < sink   or   d < band   or   (stride > 0 and d % stride == 0),
 
@@ -116,7 +118,8 @@ def template_group_bits(B, Hq, S_q, S_k, tile_m, tile_n, tiles_per_bit, sink, ba
     n_g = n_tiles(n_kt, tiles_per_bit)
     bits = np.ones((n_qt, n_g), dtype=np.uint8)
     for qt in range(n_qt):
-        gq = min(n_g - 1, ((qt + 1) * tile_m - 1) // (tiles_per_bit * tile_n))
+        pos = (qt + 1) * tile_m - 1 + S_k - S_q
+        gq = min(n_g - 1, max(0, pos // (tiles_per_bit * tile_n)))
         for g in range(n_g):
             d = abs(gq - g)
             if g < sink or d < band or (stride > 0 and d % stride == 0):

@@ -175,7 +175,7 @@ def _params(lamp, **kw):
     (dict(tile_n=128), 3),
     (dict(Hkv=3), 3),
     (dict(Hkv=0), 3),
-    (dict(S_k=200), 3),                          # causal needs S_q == S_k
+    (dict(S_k=200), 3),                          # causal needs S_q <= S_k
     (dict(in_dtype=2), 3),
     (dict(code_dtype=1), 3),
     (dict(mode=1, sub_rows=16), 3),
@@ -222,7 +222,8 @@ def test_bench_route_counts_match_oracle():
     from oracle import attention as A
     from oracle import mask as omask
     for causal, S_q, S_k, tm, G, f16 in [(True, 300, 300, 128, 2, 0.3), (False, 200, 333, 64, 1, 0.5),
-                                         (True, 512, 512, 64, 3, 0.0), (True, 256, 256, 128, 1, 1.0)]:
+                                         (True, 512, 512, 64, 3, 0.0), (True, 256, 256, 128, 1, 1.0),
+                                         (True, 200, 333, 128, 2, 0.4), (True, 1, 700, 64, 1, 0.5)]:
         rng = np.random.default_rng(S_q)
         q = rng.standard_normal((2, 3, S_q, 8))
         k = rng.standard_normal((2, 1, S_k, 8))

@@ -159,6 +159,11 @@ SMALL = [
     (128, 128, "f16", "i8", True, 1, 8, 1, 64, 64, 1, 0.5),
     (128, 128, "bf16", "i8", True, 1, 1, 1, 1, 1, 1, 0.5),
     (64, 64, "f16", "e4m3", False, 1, 1, 1, 1, 70, 1, 0.5),
+    # causal with fewer queries than keys (the queries are the last S_q positions)
+    (128, 128, "bf16", "i8", True, 1, 4, 2, 200, 333, 2, 0.3),
+    (64, 64, "f16", "e4m3", True, 1, 2, 1, 70, 300, 1, 0.5),
+    (128, 64, "bf16", "i8", True, 2, 2, 1, 1, 130, 1, 0.5),
+    (256, 128, "bf16", "i8", True, 1, 2, 1, 129, 640, 1, 0.5),
 ]
 
 
@@ -185,6 +190,7 @@ LAMP = [
     (128, 64, "f16", "e4m3", True, 1, 2, 2, 200, 200, 1, 0.2, False, True, False),
     (64, 128, "bf16", "i8", False, 1, 2, 1, 150, 260, 1, 0.3, True, True, False),
     (128, 128, "bf16", "e4m3", True, 1, 2, 2, 777, 777, 1, 0.0, True, True, True),
+    (128, 128, "bf16", "e4m3", True, 1, 2, 1, 200, 450, 1, 0.3, True, True, False),
 ]
 
 
@@ -312,27 +318,28 @@ def test_error_paths():
 # ---------------------------------------------------------------------------
 
 TEMPLATE = [
-    # D, tm, dtype, code, causal, Hq, Hkv, S, G, sink, band, stride
-    (128, 128, "bf16", "i8", True, 4, 2, 1000, 1, 1, 2, 4),
-    (64, 64, "f16", "e4m3", True, 2, 1, 700, 2, 0, 1, 3),
-    (128, 128, "bf16", "i8", False, 2, 2, 520, 1, 2, 1, 0),
+    # D, tm, dtype, code, causal, Hq, Hkv, S_q, S_k, G, sink, band, stride
+    (128, 128, "bf16", "i8", True, 4, 2, 1000, 1000, 1, 1, 2, 4),
+    (64, 64, "f16", "e4m3", True, 2, 1, 700, 700, 2, 0, 1, 3),
+    (128, 128, "bf16", "i8", False, 2, 2, 520, 520, 1, 2, 1, 0),
+    (128, 128, "bf16", "i8", True, 2, 1, 300, 900, 1, 1, 2, 3),
 ]
 
 
-@pytest.mark.parametrize("case", TEMPLATE, ids=lambda c: "d{}_m{}_{}_{}_{}_s{}_t{}.{}.{}".format(
-    c[0], c[1], c[2], c[3], "causal" if c[4] else "full", c[7], c[9], c[10], c[11]))
+@pytest.mark.parametrize("case", TEMPLATE, ids=lambda c: "d{}_m{}_{}_{}_{}_s{}x{}_t{}.{}.{}".format(
+    c[0], c[1], c[2], c[3], "causal" if c[4] else "full", c[7], c[8], c[10], c[11], c[12]))
 def test_template_tilemix(case):
     import mixed_precision_tiled_amd as L
-    D, tm, dt, code, causal, Hq, Hkv, S, G, sink, band, stride = case
-    cfg = small_cfg(D, tm, dt, code, causal, 1, Hq, Hkv, S, G, 0.5)
-    q, k, v = inputs_qk(cfg, S, S)
+    D, tm, dt, code, causal, Hq, Hkv, S_q, S_k, G, sink, band, stride = case
+    cfg = small_cfg(D, tm, dt, code, causal, 1, Hq, Hkv, max(S_q, S_k), G, 0.5)
+    q, k, v = inputs_qk(cfg, S_q, S_k)
     print(f"[attn] template {case}", flush=True)
-    n_g = -(-(-(-S // cfg.tile_n)) // G)
+    n_g = -(-(-(-S_k // cfg.tile_n)) // G)
     W = max(1, -(-n_g // 64))
-    m = L.lamp_build_mask_template(1, Hq, S, S, tm, cfg.tile_n, G, sink, band, stride, W,
+    m = L.lamp_build_mask_template(1, Hq, S_q, S_k, tm, cfg.tile_n, G, sink, band, stride, W,
                                    device=device())
     words = m.cpu().numpy().view(np.uint64)
-    ref = omask.build_mask_template(1, Hq, S, S, tm, cfg.tile_n, G, sink, band, stride, W)
+    ref = omask.build_mask_template(1, Hq, S_q, S_k, tm, cfg.tile_n, G, sink, band, stride, W)
     assert (words == ref).all()
     g = gpu_run(cfg, q, k, v, mask_words=words)
     P = oracle_problem(cfg, q, k, v, mask_words=ref)

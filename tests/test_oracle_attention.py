@@ -340,3 +340,70 @@ def test_quadratic_arithmetic_claim():
     # TileMix page, section 1: a 32,000-token document has about 1e9 score
     # interactions
     assert 32_000 * 32_000 >= 1.0e9
+
+
+# ---------------------------------------------------------------------------
+# causal with fewer queries than keys: the queries are the last S_q positions
+# ---------------------------------------------------------------------------
+
+def sdpa_bottom_right(q, k, v, sm):
+    """fp64 SDPA with an explicit mask: query i sees keys j <= i + S_k - S_q."""
+    S_q, S_k = q.shape[2], k.shape[2]
+    rep = q.shape[1] // k.shape[1]
+    kt = torch.from_numpy(k).repeat_interleave(rep, dim=1)
+    vt = torch.from_numpy(v).repeat_interleave(rep, dim=1)
+    keep = torch.arange(S_k)[None, :] <= torch.arange(S_q)[:, None] + (S_k - S_q)
+    return F.scaled_dot_product_attention(torch.from_numpy(q), kt, vt, attn_mask=keep,
+                                          scale=sm).numpy()
+
+
+def chunk_problem(seed, S_q, S_k, f16, code="i8", **kw):
+    q = rand16((1, 2, S_q, 16), seed)
+    k = rand16((1, 1, S_k, 16), seed + 1)
+    v = rand16((1, 1, S_k, 16), seed + 2)
+    return A.make_problem(q, k, v, causal=True, code=code, tile_m=32, tile_n=16,
+                          tiles_per_bit=1, frac_16bit=f16, seed=seed + 100, **kw)
+
+
+@pytest.mark.parametrize("S_q,S_k", [(40, 100), (1, 77), (64, 64)])
+def test_causal_chunk_all_16bit_is_sdpa(S_q, S_k):
+    P = chunk_problem(21, S_q, S_k, 1.0)
+    assert np.abs(full_tilemix(P) - sdpa_bottom_right(P.q, P.k, P.v, P.sm_scale)).max() < 1e-12
+
+
+def test_causal_chunk_is_suffix_of_full_prefill():
+    # the last S_q rows of a causal prefill over S_k tokens, computed as a
+    # chunk (same keys, same per-row routes), equal the full prefill's rows
+    S_k, S_q = 96, 40
+    q = rand16((1, 2, S_k, 16), 31)
+    k = rand16((1, 1, S_k, 16), 32)
+    v = rand16((1, 1, S_k, 16), 33)
+    full = A.make_problem(q, k, v, causal=True, code="i8", tile_m=8, tile_n=16,
+                          tiles_per_bit=1, frac_16bit=1.0, seed=1)
+    chunk = A.make_problem(q[:, :, S_k - S_q:].copy(), k, v, causal=True, code="i8", tile_m=8,
+                           tile_n=16, tiles_per_bit=1, frac_16bit=1.0, seed=1)
+    for h in range(2):
+        of = A.attn_tilemix(full, 0, h, np.arange(S_k - S_q, S_k))[0]
+        oc = A.attn_tilemix(chunk, 0, h, np.arange(S_q))[0]
+        assert np.abs(of - oc).max() < 1e-12
+
+
+def test_causal_chunk_brute_force():
+    P = chunk_problem(41, 10, 23, 0.5)
+    O = np.zeros(P.q.shape)
+    off = P.S_k - P.S_q
+    for h in range(P.Hq):
+        for i in range(P.S_q):
+            js = [j for j in range(P.S_k) if j <= i + off]
+            s = [brute_logit(P, 0, h, i, j)[0] for j in js]
+            m = max(s)
+            p = [math.exp(x - m) for x in s]
+            l = sum(p)
+            for d in range(P.D):
+                O[0, h, i, d] = sum(pj * P.v[0, P.kvh(h), j, d] for pj, j in zip(p, js)) / l
+    assert np.abs(full_tilemix(P) - O).max() < 1e-12
+
+
+def test_causal_more_queries_than_keys_rejected():
+    with pytest.raises(ValueError):
+        chunk_problem(1, 50, 40, 0.5)

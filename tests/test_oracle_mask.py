@@ -137,12 +137,20 @@ def test_template_extremes_and_grouping():
     bits = mask.template_group_bits(1, 1, 2048, 2048, 128, 64, 4, 0, 1, 0)[0, 0]
     for qt in range(16):
         assert bits[qt].tolist() == [0 if g == qt // 2 else 1 for g in range(8)]
-    # keys beyond the queries (S_k > S_q, non-causal use): gq clamps below n_g
+    # keys beyond the queries (a chunk of 128 queries after 896 earlier
+    # tokens): the tile's last row sits at key 1023, group 15
     bits = mask.template_group_bits(1, 1, 128, 1024, 128, 64, 1, 0, 1, 0)[0, 0]
-    assert bits.tolist() == [[1, 0] + [1] * 14]
-    # queries beyond the keys: gq clamps to the last group
+    assert bits.tolist() == [[1] * 15 + [0]]
+    # 300 queries after 212 tokens, tile_m 64, G 2 (128 keys per group):
+    # tile ends at keys 275, 339, 403, 467, 531 -> groups 2, 2, 3, 3, 4 -> 3
+    # (clamped: 4 groups)
+    bits = mask.template_group_bits(1, 1, 300, 512, 64, 64, 2, 0, 1, 0)[0, 0]
+    assert [int(np.argmin(r)) for r in bits] == [2, 2, 3, 3, 3] and (bits.sum(1) == 3).all()
+    # queries beyond the keys: positions before key 0 clamp to group 0, the
+    # others land on the last group
     bits = mask.template_group_bits(1, 1, 1024, 128, 128, 64, 1, 0, 1, 0)[0, 0]
-    assert (bits[:, 1] == 0).all() and (bits[:, 0] == 1).all()
+    assert (bits[:7, 0] == 0).all() and (bits[:7, 1] == 1).all()
+    assert bits[7].tolist() == [1, 0]
 
 
 def test_template_packing_multiword():
