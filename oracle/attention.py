@@ -36,7 +36,11 @@ Readings where the pages are silent (listed in the design notes): causal
 aligns the queries with the end of the keys, as for a chunk of S_q new
 queries after S_k - S_q earlier tokens: query i sits at key position
 i + S_k - S_q and sees keys j <= i + S_k - S_q (so S_q <= S_k; S_q == S_k is
-the plain lower triangle); GQA maps query head h to KV head
+the plain lower triangle); a variable-length batch gives each sequence b its
+own lengths Lq[b] <= S_q and Lk[b] <= S_k inside the padded tensors, rows and
+keys beyond them are padding (quantised as zeros, never attended, their
+outputs undefined), and causal alignment uses Lk[b] - Lq[b]; a row with no
+valid key has O = 0 and LSE = -inf; GQA maps query head h to KV head
 h // (Hq / Hkv); sm defaults to 1 / sqrt(D); the 8-bit logit that is rounded
 is the max-shifted x = s - m_new, then exp(x) is rounded again, both to E4M3
 with round-to-nearest-even and saturation; alpha = exp(m - m_new) is full
@@ -74,6 +78,8 @@ class Problem:
     exp8: bool = False
     tau: float = 4.0
     sub_rows: int = 32
+    seqlens_q: np.ndarray = None  # [B] lengths of a variable-length batch (None: S_q)
+    seqlens_k: np.ndarray = None  # [B] (None: S_k)
 
     def __post_init__(self):
         B, Hq, S_q, D = self.q.shape
@@ -85,6 +91,14 @@ class Problem:
         if self.sm_scale <= 0:
             self.sm_scale = 1.0 / np.sqrt(D)
         self.B, self.Hq, self.Hkv, self.S_q, self.S_k, self.D = B, Hq, Hkv, S_q, S_k, D
+        self.Lq = np.full(B, S_q) if self.seqlens_q is None else np.asarray(self.seqlens_q)
+        self.Lk = np.full(B, S_k) if self.seqlens_k is None else np.asarray(self.seqlens_k)
+        if self.Lq.shape != (B,) or self.Lk.shape != (B,):
+            raise ValueError("one length per batch entry")
+        if (self.Lq < 0).any() or (self.Lq > S_q).any() or (self.Lk < 0).any() or (self.Lk > S_k).any():
+            raise ValueError("lengths outside [0, S]")
+        if self.causal and (self.Lq > self.Lk).any():
+            raise ValueError("causal needs Lq[b] <= Lk[b]")
         self.n_qt = omask.n_tiles(S_q, self.tile_m)
         self.n_kt = omask.n_tiles(S_k, self.tile_n)
         self.n_g = omask.n_tiles(self.n_kt, self.tiles_per_bit)
@@ -100,10 +114,11 @@ class Problem:
         g = np.arange(self.n_kt) // self.tiles_per_bit
         return self.bits[b, h][:, g].astype(bool)
 
-    def valid(self, rows, cols):
-        ok = (cols[None, :] < self.S_k) & (rows[:, None] < self.S_q)
+    def valid(self, rows, cols, b=0):
+        lq, lk = int(self.Lq[b]), int(self.Lk[b])
+        ok = (cols[None, :] < lk) & (rows[:, None] < lq)
         if self.causal:
-            ok &= cols[None, :] <= rows[:, None] + (self.S_k - self.S_q)
+            ok &= cols[None, :] <= rows[:, None] + (lk - lq)
         return ok
 
 
@@ -115,8 +130,8 @@ def make_problem(q, k, v, *, causal, code, tile_m, tile_n, tiles_per_bit, frac_1
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
-    qc, qs = quant.quantize_blocks(q, tile_m, code)
-    kc, ks = quant.quantize_blocks(k, tile_n, code)
+    qc, qs = quant.quantize_blocks(q, tile_m, code, kw.get("seqlens_q"))
+    kc, ks = quant.quantize_blocks(k, tile_n, code, kw.get("seqlens_k"))
     B, Hq, S_q, _ = q.shape
     S_k = k.shape[2]
     if mask_words is None:
@@ -163,7 +178,7 @@ def routed_logits(P, b, h, rows):
     cols = np.arange(P.S_k)
     r8 = P.route8_tiles(b, h)[(rows // P.tile_m)][:, cols // P.tile_n]
     s = np.where(r8, logits8(P, b, h, rows, cols), logits16(P, b, h, rows, cols))
-    return s, r8, P.valid(rows, cols)
+    return s, r8, P.valid(rows, cols, b)
 
 
 # ---------------------------------------------------------------------------
@@ -176,10 +191,15 @@ def attn_tilemix(P, b, h, rows):
     s, _, ok = routed_logits(P, b, h, rows)
     s = np.where(ok, s, -np.inf)
     m = s.max(axis=1)
-    p = np.exp(s - m[:, None])
+    none = ~ok.any(axis=1)               # rows with no valid key: O = 0, LSE = -inf
+    m = np.where(none, 0.0, m)
+    p = np.where(ok, np.exp(s - m[:, None]), 0.0)
     l = p.sum(axis=1)
-    O = (p @ P.v[b, P.kvh(h)]) / l[:, None]
-    return O, m + np.log(l)
+    l_safe = np.where(none, 1.0, l)
+    O = (p @ P.v[b, P.kvh(h)]) / l_safe[:, None]
+    with np.errstate(divide="ignore"):
+        lse = np.where(none, -np.inf, m + np.log(l_safe))
+    return O, lse
 
 
 # ---------------------------------------------------------------------------
@@ -261,7 +281,7 @@ def attn_lamp(P, b, h, sub_blocks):
 
     for kt in range(P.n_kt):
         cols = np.arange(kt * P.tile_n, min(P.S_k, (kt + 1) * P.tile_n))
-        ok = P.valid(rows, cols)
+        ok = P.valid(rows, cols, b)
         if not ok.any():
             continue
         r8 = r8_tiles[qt, kt][:, None] & ok             # valid and 8-bit routed
@@ -324,10 +344,13 @@ def attn_lamp(P, b, h, sub_blocks):
         nflag += int((ok & r8 & flag_row[:, None]).sum())
         nvalid += int(ok.sum())
 
-    O = acc / l[:, None]
-    lse = m + np.log(l)
+    none = l == 0                        # rows with no valid key: O = 0, LSE = -inf
+    l_safe = np.where(none, 1.0, l)
+    O = acc / l_safe[:, None]
+    with np.errstate(divide="ignore"):
+        lse = np.where(none, -np.inf, m + np.log(l_safe))
     fragile_rows = diverged[sb_idx]
-    extra = (frag_pv + frag_p * np.abs(O).max(axis=1)) / l
+    extra = (frag_pv + frag_p * np.abs(O).max(axis=1)) / l_safe
     counts = dict(n8=n8, n16=n16, nflag=nflag, nvalid=nvalid)
     return LampResult(O=O, lse=lse, flags=flags, flag_dontcare=dontcare,
                       fragile_rows=fragile_rows, extra_tol=extra, counts=counts), rows, usb
@@ -349,15 +372,16 @@ def route_counts(P):
     """
     n8 = n16 = 0
     rows_all = np.arange(P.S_q)
-    for qt in range(P.n_qt):
-        rows = rows_all[qt * P.tile_m:(qt + 1) * P.tile_m]
-        for kt in range(P.n_kt):
-            cols = np.arange(kt * P.tile_n, min(P.S_k, (kt + 1) * P.tile_n))
-            nv = int(P.valid(rows, cols).sum())
-            if nv == 0:
-                continue
-            g = kt // P.tiles_per_bit
-            n8b = int(P.bits[:, :, qt, g].sum())
-            n8 += nv * n8b
-            n16 += nv * (P.B * P.Hq - n8b)
+    for b in range(P.B):
+        for qt in range(P.n_qt):
+            rows = rows_all[qt * P.tile_m:(qt + 1) * P.tile_m]
+            for kt in range(P.n_kt):
+                cols = np.arange(kt * P.tile_n, min(P.S_k, (kt + 1) * P.tile_n))
+                nv = int(P.valid(rows, cols, b).sum())
+                if nv == 0:
+                    continue
+                g = kt // P.tiles_per_bit
+                n8b = int(P.bits[b, :, qt, g].sum())
+                n8 += nv * n8b
+                n16 += nv * (P.Hq - n8b)
     return dict(n8=n8, n16=n16, nvalid=n8 + n16)

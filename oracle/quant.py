@@ -26,16 +26,27 @@ from . import e4m3
 QMAX = {"i8": 127.0, "e4m3": 448.0}
 
 
-def quantize_blocks(x, block_rows, code):
+def quantize_blocks(x, block_rows, code, lengths=None):
     """Quantise x[B, H, S, D] (values exactly representable in fp32).
 
     Returns (codes, scales): codes uint8 [B, H, S, D] (int8 two's complement or
     E4M3FN bits), scales float32 [B, H, ceil(S / block_rows)].
+
+    ``lengths`` (variable-length batch, one length per b, 0 <= L[b] <= S):
+    rows L[b] .. S-1 of sequence b are padding and count as zeros, so they do
+    not enter a block's absmax and their codes are 0.
     """
     if code not in QMAX:
         raise ValueError(code)
     x = np.asarray(x, dtype=np.float32)
     B, H, S, D = x.shape
+    if lengths is not None:
+        lengths = np.asarray(lengths)
+        if lengths.shape != (B,) or (lengths < 0).any() or (lengths > S).any():
+            raise ValueError("lengths must hold one value in [0, S] per batch entry")
+        x = x.copy()
+        for b in range(B):
+            x[b, :, int(lengths[b]):, :] = 0.0
     nb = -(-S // block_rows)
     qmax = np.float32(QMAX[code])
     codes = np.zeros((B, H, S, D), dtype=np.uint8)

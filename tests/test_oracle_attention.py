@@ -407,3 +407,94 @@ def test_causal_chunk_brute_force():
 def test_causal_more_queries_than_keys_rejected():
     with pytest.raises(ValueError):
         chunk_problem(1, 50, 40, 0.5)
+
+
+# ---------------------------------------------------------------------------
+# variable-length batches: each sequence equals its own dense problem
+# ---------------------------------------------------------------------------
+
+def varlen_problem(seed, S_q, S_k, Lq, Lk, causal, f16, code="i8", **kw):
+    B = len(Lq)
+    q = rand16((B, 2, S_q, 16), seed)
+    k = rand16((B, 1, S_k, 16), seed + 1)
+    v = rand16((B, 1, S_k, 16), seed + 2)
+    return A.make_problem(q, k, v, causal=causal, code=code, tile_m=32, tile_n=16,
+                          tiles_per_bit=2, frac_16bit=f16, seed=seed + 100,
+                          seqlens_q=np.array(Lq), seqlens_k=np.array(Lk), **kw)
+
+
+def dense_slice(P, b, **kw):
+    """Sequence b of a variable-length problem as a dense problem of its own
+    lengths, with the same mask rows."""
+    lq, lk = int(P.Lq[b]), int(P.Lk[b])
+    n_qt = -(-lq // P.tile_m)
+    return A.make_problem(P.q[b:b + 1, :, :lq], P.k[b:b + 1, :, :lk], P.v[b:b + 1, :, :lk],
+                          causal=P.causal, code=P.code, tile_m=P.tile_m, tile_n=P.tile_n,
+                          tiles_per_bit=P.tiles_per_bit, frac_16bit=0.0, seed=0,
+                          mask_words=P.mask_words[b:b + 1, :, :n_qt], sm_scale=P.sm_scale, **kw)
+
+
+@pytest.mark.parametrize("causal,Lq,Lk", [
+    (True, [70, 1, 100, 33], [100, 9, 100, 64]),
+    (False, [50, 100, 17], [3, 120, 120]),
+])
+@pytest.mark.parametrize("code", ["i8", "e4m3"])
+def test_varlen_equals_dense_sequences(causal, Lq, Lk, code):
+    P = varlen_problem(51, 100, 120, Lq, Lk, causal, 0.4, code)
+    for b in range(P.B):
+        lq = int(P.Lq[b])
+        D = dense_slice(P, b)
+        # quantiser: codes of valid rows and the scales of their blocks agree;
+        # padding rows are code 0
+        assert (P.q_codes[b, :, :lq] == D.q_codes[0]).all()
+        assert (P.q_codes[b, :, lq:] == 0).all()
+        nq = -(-lq // P.tile_m)
+        assert (P.q_scales[b, :, :nq] == D.q_scales[0]).all()
+        assert (P.q_scales[b, :, nq:] == 0).all()
+        lk = int(P.Lk[b])
+        assert (P.k_codes[b, :, :lk] == D.k_codes[0]).all() and (P.k_codes[b, :, lk:] == 0).all()
+        for h in range(P.Hq):
+            o1, l1 = A.attn_tilemix(P, b, h, np.arange(lq))
+            o2, l2 = A.attn_tilemix(D, 0, h, np.arange(lq))
+            assert np.abs(o1 - o2).max(initial=0) < 1e-12
+            assert (np.isneginf(l1) == np.isneginf(l2)).all()
+            fin = np.isfinite(l2)
+            assert np.abs(l1[fin] - l2[fin]).max(initial=0) < 1e-12
+
+
+def test_varlen_lamp_equals_dense_sequences():
+    P = varlen_problem(61, 96, 96, [96, 40, 7], [96, 80, 50], True, 0.0, "e4m3",
+                       adaptive=True, exp8=True, tau=2.0, sub_rows=16)
+    for b in range(P.B):
+        lq = int(P.Lq[b])
+        D = dense_slice(P, b, adaptive=True, exp8=True, tau=2.0, sub_rows=16)
+        nsb = -(-lq // 16)
+        for h in range(P.Hq):
+            r1, rows1, _ = A.attn_lamp(P, b, h, np.arange(nsb))
+            r2, rows2, _ = A.attn_lamp(D, 0, h, np.arange(nsb))
+            keep = rows1 < lq
+            assert (rows1[keep] == rows2).all()
+            assert np.abs(r1.O[keep] - r2.O).max() < 1e-12
+            nk = r2.flags.shape[1]
+            assert (r1.flags[:, :nk] == r2.flags).all() and not r1.flags[:, nk:].any()
+
+
+def test_varlen_full_lengths_equal_dense():
+    P = varlen_problem(71, 64, 64, [64, 64], [64, 64], True, 0.5)
+    Q = A.make_problem(P.q, P.k, P.v, causal=True, code="i8", tile_m=32, tile_n=16,
+                       tiles_per_bit=2, frac_16bit=0.5, seed=171)
+    assert (P.q_codes == Q.q_codes).all() and (P.mask_words == Q.mask_words).all()
+    for b in range(2):
+        for h in range(2):
+            assert np.abs(A.attn_tilemix(P, b, h, np.arange(64))[0] -
+                          A.attn_tilemix(Q, b, h, np.arange(64))[0]).max() == 0
+
+
+def test_varlen_rows_without_keys():
+    P = varlen_problem(81, 40, 40, [40, 20], [0, 20], False, 0.5)
+    O, lse = A.attn_tilemix(P, 0, 0, np.arange(40))
+    assert (O == 0).all() and np.isneginf(lse).all()
+    with pytest.raises(ValueError):
+        varlen_problem(1, 40, 40, [30], [20], True, 0.5)        # causal needs Lq <= Lk
+    with pytest.raises(ValueError):
+        varlen_problem(1, 40, 40, [41], [40], False, 0.5)       # beyond the padded length
