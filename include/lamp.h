@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define LAMP_ABI_VERSION 1
+#define LAMP_ABI_VERSION 2
 
 typedef enum {
   LAMP_OK = 0,
@@ -90,6 +90,24 @@ lamp_status lamp_quantize_blocks(const void* x, int32_t x_dtype, int64_t B, int6
                                  int64_t S, int64_t D, int64_t sb, int64_t sh, int64_t ss,
                                  int32_t block_rows, int32_t code_dtype, void* codes,
                                  float* scales, void* stream);
+
+/*
+ * lamp_quantize_blocks_varlen -- lamp_quantize_blocks over a variable-length
+ * batch.
+ *
+ * Source: TileMix page, section 4 (variable-length batches), with the
+ * quantiser of section 2.  seqlens [B] int32 (device, 4-byte aligned; NULL =
+ * every sequence has length S): sequence b occupies rows 0 .. L-1 of its
+ * padded [S, D] slice, L = seqlens[b] clamped to [0, S].  Rows L .. S-1 are
+ * padding: they are not read, count as zeros for the block absmax, and get
+ * code 0 (a block wholly in the padding gets scale 0).  Everything else as
+ * for lamp_quantize_blocks.
+ */
+lamp_status lamp_quantize_blocks_varlen(const void* x, int32_t x_dtype, int64_t B, int64_t H,
+                                        int64_t S, int64_t D, int64_t sb, int64_t sh,
+                                        int64_t ss, const int32_t* seqlens, int32_t block_rows,
+                                        int32_t code_dtype, void* codes, float* scales,
+                                        void* stream);
 
 /*
  * lamp_build_mask -- the random packed precision mask.
@@ -182,6 +200,14 @@ lamp_status lamp_build_mask_template(int64_t B, int64_t Hq, int64_t S_q, int64_t
  *   dbg_qk_acc [B, Hq, S_q, S_k] int32, int8 path only: the raw int32 QK^T
  *              accumulators of every 8-bit key tile a 32-row wave computes
  *              (tiny shapes; other entries are left untouched).
+ * Variable-length batch (TileMix section 4; NULL = all lengths S_q / S_k):
+ *   seqlens_q, seqlens_k [B] int32 (device, 4-byte aligned): sequence b has
+ *   Lq = seqlens_q[b] queries and Lk = seqlens_k[b] keys (clamped to [0, S_q]
+ *   and [0, S_k]) at the start of its padded slices; the codes and scales
+ *   must come from lamp_quantize_blocks_varlen with the same lengths.
+ *   valid(i, j) then reads j < Lk, and j <= i + Lk - Lq when causal (the
+ *   caller keeps Lq <= Lk).  A row with no valid key gets O = 0 and LSE =
+ *   -inf.  Rows i >= Lq of out, lse and flags_out are not written.
  */
 typedef struct {
   uint32_t struct_size;     /* = sizeof(lamp_attn_params); ABI guard         */
@@ -209,6 +235,8 @@ typedef struct {
   float* lse;               /* optional                                      */
   uint64_t* flags_out;      /* optional, ADAPTIVE                            */
   int32_t* dbg_qk_acc;      /* optional, int8 path                           */
+  const int32_t* seqlens_q; /* optional [B], variable-length batch           */
+  const int32_t* seqlens_k; /* optional [B]                                  */
 } lamp_attn_params;
 
 lamp_status lamp_attn_fwd(const lamp_attn_params* p, void* stream);

@@ -115,22 +115,29 @@ void attn_fwd_kernel(const AttnArgs a) {
   const int b = grp / a.Hkv, kvh = grp % a.Hkv;
   const int h = kvh * a.heads_per_group + hh;
 
+  // lengths of this batch entry's sequence (a variable-length batch lives in
+  // padded tensors); a query tile wholly in the padding has nothing to do
+  const int Lq = a.seqlens_q != nullptr ? min(max(ld_uniform(a.seqlens_q + b), 0), a.S_q) : a.S_q;
+  const int Lk = a.seqlens_k != nullptr ? min(max(ld_uniform(a.seqlens_k + b), 0), a.S_k) : a.S_k;
+  if (qt * SH::TM >= Lq) return;
+
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int lr = lane & 31, hf = lane >> 5;
   const int row0 = qt * SH::TM + w * 32;
   const int my_row = row0 + lr;
-  const bool wave_live = row0 < a.S_q;
-  const int q_row = min(my_row, a.S_q - 1);
+  const bool wave_live = row0 < Lq;
+  const int q_row = min(my_row, Lq - 1);
 
   // causal: query row i sits at key position i + coff and sees keys up to it
-  const int coff = a.S_k - a.S_q;
-  const int wg_last = min(a.S_q, (qt + 1) * SH::TM) - 1;
-  const int kt_end = a.causal ? min(a.n_kt, (wg_last + coff) / 64 + 1) : a.n_kt;
-  const int w_last = min(a.S_q, row0 + 32) - 1;
-  const int kt_end_w = !wave_live ? 0 : (a.causal ? min(a.n_kt, (w_last + coff) / 64 + 1) : a.n_kt);
-  const bool rows_ragged = row0 + 32 > a.S_q;
-  // largest valid key index of this lane's row (-1: row beyond S_q)
-  const int key_lim = my_row >= a.S_q ? -1 : (a.causal ? min(my_row + coff, a.S_k - 1) : a.S_k - 1);
+  const int coff = Lk - Lq;
+  const int n_kt_seq = (Lk + SH::TN - 1) / SH::TN;
+  const int wg_last = min(Lq, (qt + 1) * SH::TM) - 1;
+  const int kt_end = a.causal ? min(n_kt_seq, (wg_last + coff) / 64 + 1) : n_kt_seq;
+  const int w_last = min(Lq, row0 + 32) - 1;
+  const int kt_end_w = !wave_live ? 0 : (a.causal ? min(n_kt_seq, (w_last + coff) / 64 + 1) : n_kt_seq);
+  const bool rows_ragged = row0 + 32 > Lq;
+  // largest valid key index of this lane's row (-1: padding row)
+  const int key_lim = my_row >= Lq ? -1 : (a.causal ? min(my_row + coff, Lk - 1) : Lk - 1);
 
   // ---- Q fragments (B operand of S^T = K Q^T), resident for the whole loop
   const char* qp = reinterpret_cast<const char*>(a.q) +
@@ -159,7 +166,7 @@ void attn_fwd_kernel(const AttnArgs a) {
   const uint8_t* k8base = a.k8 + ((int64_t)b * a.Hkv + kvh) * a.S_k * D;
   const float* sKp = a.k_scale + ((int64_t)b * a.Hkv + kvh) * a.n_kt;
   const uint32_t kss = 2u * (uint32_t)a.k_ss, vss = 2u * (uint32_t)a.v_ss;
-  const int key_max = a.S_k - 1;
+  const int key_max = Lk - 1;
 
   auto tile_is8 = [&](int kt) -> bool {
     const int g = kt / a.tiles_per_bit;
@@ -192,9 +199,9 @@ void attn_fwd_kernel(const AttnArgs a) {
   // first row and end with the head's last row: per-lane offsets past S_k
   // (ragged last tile) fall outside the resource and read zeros, which are
   // never valid logits
-  const uint32_t k16_bytes = (uint32_t)(a.S_k - 1) * kss + 2u * D;
-  const uint32_t k8_bytes = (uint32_t)a.S_k * D;
-  const uint32_t v_bytes = (uint32_t)(a.S_k - 1) * vss + 2u * D;
+  const uint32_t k16_bytes = Lk > 0 ? (uint32_t)(Lk - 1) * kss + 2u * D : 0u;
+  const uint32_t k8_bytes = (uint32_t)Lk * D;
+  const uint32_t v_bytes = Lk > 0 ? (uint32_t)(Lk - 1) * vss + 2u * D : 0u;
   auto issue_k = [&](int kt, bool is8, char* kdst) {
     const uint32_t key0 = (uint32_t)(kt * SH::TN);
     if (is8) {
@@ -330,12 +337,12 @@ void attn_fwd_kernel(const AttnArgs a) {
         acc[1] = mfma_i8(kf1[t], q8[t], acc[1]);
       }
       if constexpr (DBG) {
-        if (my_row < a.S_q) {
+        if (my_row < Lq) {
           int32_t* dr = a.dbg + (((int64_t)b * a.Hq + h) * a.S_q + my_row) * a.S_k;
 #pragma unroll
           for (int e = 0; e < 32; ++e) {
             const int j = key0 + kofs(e) + 4 * hf;
-            if (j < a.S_k) dr[j] = acc[e >> 4][e & 15] - init;
+            if (j < Lk) dr[j] = acc[e >> 4][e & 15] - init;
           }
         }
       }
@@ -365,7 +372,7 @@ void attn_fwd_kernel(const AttnArgs a) {
   };
   auto qk_part = [&](int kt, const char* kb, bool is8, float sK, float* x) -> Logits {
     const int key0 = kt * SH::TN;
-    const bool need_mask = rows_ragged || (key0 + SH::TN > a.S_k) ||
+    const bool need_mask = rows_ragged || (key0 + SH::TN > Lk) ||
                            (a.causal && key0 + SH::TN - 1 > row0 + coff);
     // valid(e) <=> kofs(e) <= lim_rel
     const int lim_rel = key_lim - key0 - 4 * hf;
@@ -598,8 +605,9 @@ void attn_fwd_kernel(const AttnArgs a) {
   }
   // ---- epilogue: O = acc / l, 16-bit store, optional LSE ----
   const float l_tot = halves_sum(l_run);
-  if (wave_live && my_row < a.S_q) {
-    const float inv_l = 1.f / l_tot;
+  if (wave_live && my_row < Lq) {
+    // a row without any valid key (variable-length batch) gets O = 0
+    const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
     char* op = reinterpret_cast<char*>(a.out) +
                2 * (b * a.o_sb + h * a.o_sh + (int64_t)my_row * a.o_ss);
 #pragma unroll
@@ -614,7 +622,7 @@ void attn_fwd_kernel(const AttnArgs a) {
     }
     if (a.lse != nullptr && hf == 0) {
       const float lg = __builtin_amdgcn_logf(l_tot);      // log2
-      const float lse = LAZY ? (m_run + lg) * kLn2 : m_run + lg * kLn2;
+      const float lse = l_tot > 0.f ? (LAZY ? (m_run + lg) * kLn2 : m_run + lg * kLn2) : kNegInf;
       a.lse[((int64_t)b * a.Hq + h) * a.S_q + my_row] = lse;
     }
   }

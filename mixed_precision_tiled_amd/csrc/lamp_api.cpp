@@ -67,6 +67,15 @@ lamp_status lamp_quantize_blocks(const void* x, int32_t x_dtype, int64_t B, int6
                                  int64_t D, int64_t sb, int64_t sh, int64_t ss,
                                  int32_t block_rows, int32_t code_dtype, void* codes,
                                  float* scales, void* stream) {
+  return lamp_quantize_blocks_varlen(x, x_dtype, B, H, S, D, sb, sh, ss, nullptr, block_rows,
+                                     code_dtype, codes, scales, stream);
+}
+
+lamp_status lamp_quantize_blocks_varlen(const void* x, int32_t x_dtype, int64_t B, int64_t H,
+                                        int64_t S, int64_t D, int64_t sb, int64_t sh,
+                                        int64_t ss, const int32_t* seqlens, int32_t block_rows,
+                                        int32_t code_dtype, void* codes, float* scales,
+                                        void* stream) {
   if (B < 0 || H < 0 || S < 0 || D < 0) return fail(LAMP_ERR_SHAPE, "negative size");
   if (sb < 0 || sh < 0 || ss < 0) return fail(LAMP_ERR_SHAPE, "negative stride");
   if (!is16(x_dtype)) return fail(LAMP_ERR_UNSUPPORTED, "x_dtype must be LAMP_F16 or LAMP_BF16");
@@ -80,6 +89,7 @@ lamp_status lamp_quantize_blocks(const void* x, int32_t x_dtype, int64_t B, int6
   if (ss < D) return fail(LAMP_ERR_SHAPE, "row stride %lld < D", (long long)ss);
   if (!aligned16(x) || !aligned16(codes) || (ss % 8) || (sh % 8) || (sb % 8))
     return fail(LAMP_ERR_ALIGN, "x, codes need 16-byte alignment and strides a multiple of 8");
+  if (reinterpret_cast<uintptr_t>(seqlens) & 3u) return fail(LAMP_ERR_ALIGN, "seqlens needs 4-byte alignment");
   const int64_t nb = cdiv(S, block_rows);
   if (B * H * nb > kMaxGrid) return fail(LAMP_ERR_UNSUPPORTED, "too many blocks");
   lamp::QuantArgs a{};
@@ -95,6 +105,7 @@ lamp_status lamp_quantize_blocks(const void* x, int32_t x_dtype, int64_t B, int6
   a.D = (int32_t)D;
   a.block_rows = block_rows;
   a.nb = (int32_t)nb;
+  a.seqlens = seqlens;
   a.bf16 = x_dtype == LAMP_BF16;
   a.e4m3 = code_dtype == LAMP_E4M3;
   return hip_status(lamp::launch_quantize(a, static_cast<hipStream_t>(stream)), "quantize launch");
@@ -222,6 +233,8 @@ lamp_status lamp_attn_fwd(const lamp_attn_params* p, void* stream) {
       return fail(LAMP_ERR_ALIGN, "strides must be multiples of 8 elements");
   }
   if (reinterpret_cast<uintptr_t>(p->mask) & 7u) return fail(LAMP_ERR_ALIGN, "mask alignment");
+  if ((reinterpret_cast<uintptr_t>(p->seqlens_q) | reinterpret_cast<uintptr_t>(p->seqlens_k)) & 3u)
+    return fail(LAMP_ERR_ALIGN, "seqlens need 4-byte alignment");
   if (p->flags_out && (reinterpret_cast<uintptr_t>(p->flags_out) & 7u))
     return fail(LAMP_ERR_ALIGN, "flags_out alignment");
   if (p->B * p->Hq * n_qt > kMaxGrid) return fail(LAMP_ERR_UNSUPPORTED, "grid too large");
@@ -242,6 +255,8 @@ lamp_status lamp_attn_fwd(const lamp_attn_params* p, void* stream) {
   a.lse = p->lse;
   a.flags = p->mode == LAMP_MODE_ADAPTIVE ? p->flags_out : nullptr;
   a.dbg = p->dbg_qk_acc;
+  a.seqlens_q = p->seqlens_q;
+  a.seqlens_k = p->seqlens_k;
   a.q_sb = p->q_str[0];
   a.q_sh = p->q_str[1];
   a.q_ss = p->q_str[2];

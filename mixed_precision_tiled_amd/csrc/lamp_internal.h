@@ -15,6 +15,7 @@ struct QuantArgs {
   int64_t sb, sh, ss;          // element strides of x
   int32_t B, H, S, D;
   int32_t block_rows, nb;      // nb = ceil(S / block_rows)
+  const int32_t* seqlens;      // [B] or nullptr (all S)
   bool bf16, e4m3;
 };
 
@@ -52,6 +53,8 @@ struct AttnArgs {
   float* lse;
   uint64_t* flags;
   int32_t* dbg;
+  const int32_t* seqlens_q;    // [B] or nullptr (all S_q)
+  const int32_t* seqlens_k;    // [B] or nullptr (all S_k)
   int64_t q_sb, q_sh, q_ss;
   int64_t k_sb, k_sh, k_ss;
   int64_t v_sb, v_sh, v_ss;

@@ -27,6 +27,9 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantArgs a) {
   const int b = bh / a.H;
   const int r0 = blk * a.block_rows;
   const int rows = min(a.block_rows, a.S - r0);
+  // rows at or past the sequence length are padding: not read, zero
+  const int len = a.seqlens != nullptr ? min(max(ld_uniform(a.seqlens + b), 0), a.S) : a.S;
+  const int rows_live = min(rows, max(len - r0, 0));
   const int cpr = a.D / 8;                      // 8-element chunks per row
   const int nch = rows * cpr;
   const char* base = reinterpret_cast<const char*>(a.x) +
@@ -38,7 +41,8 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantArgs a) {
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const int c = tid + i * kQuantThreads;
-    if (c < nch) {
+    cache[i] = u32x4{0u, 0u, 0u, 0u};
+    if (c < nch && c / cpr < rows_live) {
       const int r = c / cpr, col = (c % cpr) * 8;
       cache[i] = ld_global16(base + 2 * ((int64_t)r * a.ss + col));
 #pragma unroll

@@ -51,12 +51,16 @@ class lamp_attn_params(ctypes.Structure):
         ("words_per_row", _i32), ("tile_m", _i32), ("tile_n", _i32), ("tiles_per_bit", _i32),
         ("exp8", _i32), ("tau", ctypes.c_float), ("sub_rows", _i32),
         ("out", _vp), ("lse", _vp), ("flags_out", _vp), ("dbg_qk_acc", _vp),
+        ("seqlens_q", _vp), ("seqlens_k", _vp),
     ]
 
 
 _lib.lamp_quantize_blocks.restype = _i32
 _lib.lamp_quantize_blocks.argtypes = [_vp, _i32, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i32,
                                       _i32, _vp, _vp, _vp]
+_lib.lamp_quantize_blocks_varlen.restype = _i32
+_lib.lamp_quantize_blocks_varlen.argtypes = [_vp, _i32, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                             _vp, _i32, _i32, _vp, _vp, _vp]
 _lib.lamp_build_mask.restype = _i32
 _lib.lamp_build_mask.argtypes = [_i64, _i64, _i64, _i64, _i32, _i32, _i32, ctypes.c_double, _u64,
                                  _vp, _i32, _vp]
@@ -124,10 +128,12 @@ def cdiv(a, b):
     return -(-a // b)
 
 
-def lamp_quantize_blocks(x, block_rows, code, codes=None, scales=None):
+def lamp_quantize_blocks(x, block_rows, code, codes=None, scales=None, seqlens=None):
     """Per-block quantisation of x [B, H, S, D] (fp16/bf16 CUDA tensor).
 
     Returns (codes uint8 [B, H, S, D], scales float32 [B, H, ceil(S/block_rows)]).
+    seqlens: optional int32 tensor [B] (variable-length batch; rows past a
+    sequence's length are padding, quantised as zeros).
     """
     B, H, S, D = x.shape
     nb = cdiv(S, block_rows)
@@ -139,9 +145,12 @@ def lamp_quantize_blocks(x, block_rows, code, codes=None, scales=None):
         raise TypeError("x must be float16 or bfloat16")
     if x.stride(3) != 1 or not codes.is_contiguous() or not scales.is_contiguous():
         raise ValueError("x needs a contiguous head dim; codes and scales must be contiguous")
-    _check(_lib.lamp_quantize_blocks(_ptr(x), _DT16[x.dtype], B, H, S, D, x.stride(0), x.stride(1),
-                                     x.stride(2), block_rows, _CODE[code], _ptr(codes),
-                                     _ptr(scales), _stream(x)))
+    if seqlens is not None and (seqlens.dtype != torch.int32 or tuple(seqlens.shape) != (B,)
+                                or not seqlens.is_contiguous()):
+        raise ValueError("seqlens must be a contiguous int32 tensor [B]")
+    _check(_lib.lamp_quantize_blocks_varlen(_ptr(x), _DT16[x.dtype], B, H, S, D, x.stride(0),
+                                            x.stride(1), x.stride(2), _ptr(seqlens), block_rows,
+                                            _CODE[code], _ptr(codes), _ptr(scales), _stream(x)))
     return codes, scales
 
 
@@ -181,10 +190,11 @@ def lamp_build_mask_template(B, Hq, S_q, S_k, tile_m, tile_n, tiles_per_bit, sin
 def lamp_attn_fwd(q, k, v, q8, k8, q_scale, k_scale, mask, *, code, causal, tile_m,
                   tiles_per_bit, tile_n=64, words_per_row=None, mode=LAMP_MODE_MASK, exp8=False,
                   tau=4.0, sub_rows=32, sm_scale=0.0, out=None, lse=None, flags_out=None,
-                  dbg_qk_acc=None):
+                  dbg_qk_acc=None, seqlens_q=None, seqlens_k=None):
     """Dual-path attention forward.  q [B,Hq,S_q,D], k/v [B,Hkv,S_k,D] 16-bit,
     q8/k8 codes and q_scale/k_scale from lamp_quantize_blocks, mask from
-    lamp_build_mask.  Returns out [B,Hq,S_q,D] (q's dtype)."""
+    lamp_build_mask.  Returns out [B,Hq,S_q,D] (q's dtype).  seqlens_q /
+    seqlens_k: optional int32 tensors [B] of a variable-length batch."""
     B, Hq, S_q, D = q.shape
     _, Hkv, S_k, _ = k.shape
     if q.dtype not in _DT16 or k.dtype != q.dtype or v.dtype != q.dtype:
@@ -192,9 +202,12 @@ def lamp_attn_fwd(q, k, v, q8, k8, q_scale, k_scale, mask, *, code, causal, tile
     if out is None:
         out = torch.empty((B, Hq, S_q, D), dtype=q.dtype, device=q.device)
     W = words_per_row or mask.shape[-1]
-    for t in (q8, k8, q_scale, k_scale, mask, lse, flags_out, dbg_qk_acc):
+    for t in (q8, k8, q_scale, k_scale, mask, lse, flags_out, dbg_qk_acc, seqlens_q, seqlens_k):
         if t is not None and not t.is_contiguous():
             raise ValueError("codes, scales, mask and optional outputs must be contiguous")
+    for t in (seqlens_q, seqlens_k):
+        if t is not None and (t.dtype != torch.int32 or tuple(t.shape) != (B,)):
+            raise ValueError("seqlens must be int32 tensors [B]")
     p = lamp_attn_params()
     p.struct_size = ctypes.sizeof(lamp_attn_params)
     p.mode = mode
@@ -217,6 +230,8 @@ def lamp_attn_fwd(q, k, v, q8, k8, q_scale, k_scale, mask, *, code, causal, tile
     p.lse = None if lse is None else lse.data_ptr()
     p.flags_out = None if flags_out is None else flags_out.data_ptr()
     p.dbg_qk_acc = None if dbg_qk_acc is None else dbg_qk_acc.data_ptr()
+    p.seqlens_q = None if seqlens_q is None else seqlens_q.data_ptr()
+    p.seqlens_k = None if seqlens_k is None else seqlens_k.data_ptr()
     _check(_lib.lamp_attn_fwd(ctypes.byref(p), _stream(q)))
     return out
 

@@ -78,7 +78,7 @@ def test_library_exports_every_declared_symbol(lamp):
 
 
 def test_abi_version_and_status_strings(lamp):
-    assert lamp.lamp_abi_version() == 1
+    assert lamp.lamp_abi_version() == 2
     for i, n in enumerate(["LAMP_OK", "LAMP_ERR_NULL", "LAMP_ERR_SHAPE", "LAMP_ERR_UNSUPPORTED",
                            "LAMP_ERR_ALIGN", "LAMP_ERR_HIP"]):
         assert lamp.lamp_status_string(i) == n
@@ -127,6 +127,17 @@ def test_mask_validation(lamp):
     assert f(1, 1, 256, 256, 64, 64, 1, 0.5, 0, None, 1, None) == 1
     assert f(1, 1, 256, 256, 64, 64, 1, 0.5, 0, ctypes.c_void_p(65), 1, None) == 4
     assert f(0, 1, 256, 256, 64, 64, 1, 0.5, 0, None, 1, None) == 0
+
+
+def test_quantize_varlen_validation(lamp):
+    f = _lib(lamp).lamp_quantize_blocks_varlen
+    p = ctypes.c_void_p(16)
+    # misaligned lengths pointer
+    assert f(p, 1, 1, 1, 64, 128, 0, 0, 128, ctypes.c_void_p(18), 64, 2, p, p, None) == 4
+    # the dense checks still apply
+    assert f(p, 1, 1, 1, 64, 96, 0, 0, 96, None, 64, 2, p, p, None) == 3
+    assert f(None, 1, 1, 1, 64, 128, 0, 0, 128, p, 64, 2, p, p, None) == 1
+    assert f(None, 1, 1, 1, 0, 128, 0, 0, 128, p, 64, 2, None, None, None) == 0
 
 
 def test_mask_template_validation(lamp):
@@ -192,6 +203,8 @@ def _params(lamp, **kw):
     (dict(q=4100), 4),
     (dict(code_dtype=3, dbg_qk_acc=4096), 3),    # int32 dump exists on the int8 path only
     (dict(causal=0, S_k=0), 2),
+    (dict(seqlens_q=4098), 4),                   # lengths need 4-byte alignment
+    (dict(seqlens_k=4097), 4),
     (dict(S_q=0, S_k=0), 0),                     # empty: OK, nothing launched
     (dict(B=0), 0),
 ])

@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import device, gpu_run, oracle_mask, oracle_problem
+from gpu_util import device, gpu_run, oracle_mask, oracle_problem, u64
 from oracle import attention as A
 from oracle import compare
 from oracle import mask as omask
@@ -346,3 +346,94 @@ def test_template_tilemix(case):
     check_codes_and_mask(cfg, P, g)
     for h in range(Hq):
         check_head(cfg, P, g, 0, h)
+
+
+# ---------------------------------------------------------------------------
+# variable-length batches: per-sequence lengths inside padded tensors; the
+# padding holds NaN on the GPU side (never read) and zeros for the oracle
+# ---------------------------------------------------------------------------
+
+VARLEN = [
+    # D, tm, dtype, code, causal, Hq, Hkv, S_q, S_k, G, f16, Lq, Lk, exp8, adaptive
+    (128, 128, "bf16", "i8", True, 4, 2, 333, 333, 2, 0.3, [333, 200, 1], [333, 260, 64],
+     False, False),
+    (64, 64, "f16", "e4m3", False, 2, 1, 300, 300, 1, 0.5, [300, 0, 77], [150, 300, 0],
+     False, False),
+    (256, 128, "bf16", "i8", True, 2, 1, 260, 400, 1, 0.5, [260, 5], [400, 130], False, False),
+    (128, 128, "bf16", "e4m3", True, 2, 1, 300, 300, 1, 0.3, [300, 130], [300, 290], True, True),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN, ids=lambda c: "d{}_m{}_{}_{}_{}_Lq{}_Lk{}_x8{}_ad{}".format(
+    c[0], c[1], c[2], c[3], "causal" if c[4] else "full", "-".join(map(str, c[11])),
+    "-".join(map(str, c[12])), int(c[13]), int(c[14])))
+def test_varlen(case):
+    import mixed_precision_tiled_amd as L
+    D, tm, dt, code, causal, Hq, Hkv, S_q, S_k, G, f16, Lq, Lk, exp8, ad = case
+    B = len(Lq)
+    cfg = small_cfg(D, tm, dt, code, causal, B, Hq, Hkv, max(S_q, S_k), G, f16, exp8=exp8,
+                    adaptive=ad)
+    q, k, v = inputs_qk(cfg, S_q, S_k)
+    print(f"[attn] varlen {case}", flush=True)
+    q0, k0, v0 = q.clone(), k.clone(), v.clone()
+    for b in range(B):
+        for t, t0, n in ((q, q0, Lq[b]), (k, k0, Lk[b]), (v, v0, Lk[b])):
+            t[b, :, n:] = float("nan")
+            t0[b, :, n:] = 0.0
+    dev = device()
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    lq = torch.tensor(Lq, dtype=torch.int32, device=dev)
+    lk = torch.tensor(Lk, dtype=torch.int32, device=dev)
+    q8, sq = L.lamp_quantize_blocks(qd, tm, code, seqlens=lq)
+    k8, sk = L.lamp_quantize_blocks(kd, 64, code, seqlens=lk)
+    n_g = -(-(-(-S_k // 64)) // G)
+    W = max(1, -(-n_g // 64))
+    mask = L.lamp_build_mask(B, Hq, S_q, S_k, tm, 64, G, f16, cfg.mask_seed, W, device=dev)
+    lse = torch.full((B, Hq, S_q), float("nan"), device=dev)
+    flags = None
+    if ad:
+        flags = torch.full(L.lamp.flags_shape(B, Hq, S_q, S_k), -1, dtype=torch.int64, device=dev)
+    out = L.lamp_attn_fwd(qd, kd, vd, q8, k8, sq, sk, mask, code=code, causal=causal,
+                          tile_m=tm, tiles_per_bit=G,
+                          mode=L.LAMP_MODE_ADAPTIVE if ad else L.LAMP_MODE_MASK, exp8=exp8,
+                          tau=cfg.tau, sub_rows=32, lse=lse, flags_out=flags,
+                          seqlens_q=lq, seqlens_k=lk)
+    torch.cuda.synchronize()
+    P = A.make_problem(q0.double().numpy(), k0.double().numpy(), v0.double().numpy(),
+                       causal=causal, code=code, tile_m=tm, tile_n=64, tiles_per_bit=G,
+                       frac_16bit=f16, seed=cfg.mask_seed, words_per_row=W,
+                       seqlens_q=np.array(Lq), seqlens_k=np.array(Lk), adaptive=ad, exp8=exp8,
+                       tau=cfg.tau, sub_rows=32)
+    assert (q8.cpu().numpy() == P.q_codes).all() and (sq.cpu().numpy() == P.q_scales).all()
+    assert (k8.cpu().numpy() == P.k_codes).all() and (sk.cpu().numpy() == P.k_scales).all()
+    got, glse = out.float().cpu().numpy(), lse.cpu().numpy()
+    gflags = None if flags is None else u64(flags)
+    u16 = 2.0 ** -8 if dt == "bf16" else 2.0 ** -11
+    for b in range(B):
+        if Lq[b] == 0:
+            continue
+        for h in range(Hq):
+            if A.uses_lamp(P):
+                nsb = -(-Lq[b] // 32)
+                res, rr, usb = A.attn_lamp(P, b, h, np.arange(nsb))
+                keep = rr < Lq[b]
+                rows, O_ref, lse_ref = rr[keep], res.O[keep], res.lse[keep]
+                st = compare.check(got[b, h][rows], O_ref, dt, extra_row=res.extra_tol[keep],
+                                   exclude_rows=res.fragile_rows[keep])
+                if ad:
+                    n_kt = P.n_kt
+                    gb = omask.unpack_bits(gflags[b, h], gflags.shape[-1] * 64)[:, :n_kt]
+                    mism = (gb[usb].astype(bool) != res.flags) & ~res.flag_dontcare
+                    assert not mism.any()
+            else:
+                rows = np.arange(Lq[b])
+                O_ref, lse_ref = A.attn_tilemix(P, b, h, rows)
+                st = compare.check(got[b, h][rows], O_ref, dt)
+            assert st["ok"], f"varlen ({b},{h}): {st}"
+            none = np.isneginf(lse_ref)
+            lg = glse[b, h][rows]
+            assert np.isneginf(lg[none]).all() and (got[b, h][rows][none] == 0).all()
+            assert np.isfinite(lg[~none]).all()
+            assert np.abs(lg[~none] - lse_ref[~none]).max(initial=0) <= (
+                1e-3 + u16 + 1e-5 * np.abs(lse_ref[~none]).max(initial=0) +
+                (0.05 if A.uses_lamp(P) else 0.0))
