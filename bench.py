@@ -77,23 +77,38 @@ def tile_valid_counts(S_q, S_k, tile_m, tile_n, causal):
     return cnt
 
 
-def route_counts(mask_words, S_q, S_k, tile_m, tile_n, tiles_per_bit, causal, flags=None):
-    """dict(n8, n16, nflag, nvalid) from packed mask words [B, Hq, n_qt, W]."""
+def route_counts(mask_words, S_q, S_k, tile_m, tile_n, tiles_per_bit, causal, flags=None,
+                 seqlens_q=None, seqlens_k=None):
+    """dict(n8, n16, nflag, nvalid) from packed mask words [B, Hq, n_qt, W]
+    (optionally a variable-length batch: per-sequence lengths [B])."""
     mw = np.asarray(mask_words, dtype=np.uint64)
-    n_kt = -(-S_k // tile_n)
+    B = mw.shape[0]
+    n_qt, n_kt = -(-S_q // tile_m), -(-S_k // tile_n)
+    n_sb = -(-S_q // 32)
     g = np.arange(n_kt) // tiles_per_bit
     bits = ((mw[..., g // 64] >> (g % 64).astype(np.uint64)) & np.uint64(1)).astype(np.int64)
-    cnt = tile_valid_counts(S_q, S_k, tile_m, tile_n, causal)       # [n_qt, n_kt]
-    n8 = int((bits * cnt[None, None]).sum())
-    nvalid = int(cnt.sum()) * mw.shape[0] * mw.shape[1]
+    Lq = [S_q] * B if seqlens_q is None else [int(x) for x in seqlens_q]
+    Lk = [S_k] * B if seqlens_k is None else [int(x) for x in seqlens_k]
+
+    def counts(lq, lk, rows):
+        # [ceil(S_q/rows), n_kt] valid pairs per tile of a sequence of lengths lq, lk
+        c = np.zeros((-(-S_q // rows), n_kt), dtype=np.int64)
+        if lq > 0 and lk > 0:
+            t = tile_valid_counts(lq, lk, rows, tile_n, causal)
+            c[:t.shape[0], :t.shape[1]] = t
+        return c
+
+    cnt = np.stack([counts(Lq[b], Lk[b], tile_m) for b in range(B)])     # [B, n_qt, n_kt]
+    n8 = int((bits * cnt[:, None]).sum())
+    nvalid = int(cnt.sum()) * mw.shape[1]
     nflag = 0
     if flags is not None:
         # flags [B, Hq, n_sb, FW]: sub-block of 32 rows x key tile
         fw = np.asarray(flags, dtype=np.uint64)
         kt = np.arange(n_kt)
         fb = ((fw[..., kt // 64] >> (kt % 64).astype(np.uint64)) & np.uint64(1)).astype(np.int64)
-        sub = tile_valid_counts(S_q, S_k, 32, tile_n, causal)         # [n_sb, n_kt]
-        nflag = int((fb * sub[None, None]).sum())
+        sub = np.stack([counts(Lq[b], Lk[b], 32) for b in range(B)])    # [B, n_sb, n_kt]
+        nflag = int((fb[:, :, :n_sb] * sub[:, None]).sum())
     return dict(n8=n8, n16=nvalid - n8, nflag=nflag, nvalid=nvalid)
 
 
@@ -223,9 +238,12 @@ def cpu_baseline(cfg, q, k, v, budget_s=12.0):
 class Pipeline:
     """Preallocated buffers for one configuration; run() enqueues one step."""
 
-    def __init__(self, L, cfg, qd, kd, vd, torch, template=None):
+    def __init__(self, L, cfg, qd, kd, vd, torch, template=None, seqlens=None):
         self.L, self.cfg, self.torch = L, cfg, torch
         self.template = template       # (sink, band, stride) groups, or the random mask
+        # variable-length batch: one length per sequence (queries = keys)
+        self.seqlens = None if seqlens is None else \
+            torch.tensor(list(seqlens), dtype=torch.int32, device=qd.device)
         self.qd, self.kd, self.vd = qd, kd, vd
         dev = qd.device
         B, Hq, Hkv, S, D = cfg.B, cfg.Hq, cfg.Hkv, cfg.S, cfg.D
@@ -242,8 +260,10 @@ class Pipeline:
 
     def prep(self):
         L, c = self.L, self.cfg
-        L.lamp_quantize_blocks(self.qd, c.tile_m, c.code, codes=self.q8, scales=self.sq)
-        L.lamp_quantize_blocks(self.kd, c.tile_n, c.code, codes=self.k8, scales=self.sk)
+        L.lamp_quantize_blocks(self.qd, c.tile_m, c.code, codes=self.q8, scales=self.sq,
+                               seqlens=self.seqlens)
+        L.lamp_quantize_blocks(self.kd, c.tile_n, c.code, codes=self.k8, scales=self.sk,
+                               seqlens=self.seqlens)
         if self.template is not None:
             L.lamp_build_mask_template(c.B, c.Hq, c.S, c.S, c.tile_m, c.tile_n, c.tiles_per_bit,
                                        *self.template, c.words_per_row, mask=self.mask)
@@ -258,13 +278,14 @@ class Pipeline:
                         tiles_per_bit=c.tiles_per_bit, words_per_row=c.words_per_row,
                         mode=L.LAMP_MODE_ADAPTIVE if c.adaptive else L.LAMP_MODE_MASK,
                         exp8=c.exp8, tau=c.tau, sub_rows=c.sub_rows, out=self.out,
-                        flags_out=self.flags)
+                        flags_out=self.flags, seqlens_q=self.seqlens, seqlens_k=self.seqlens)
 
     def counts(self):
         mw = self.mask.cpu().numpy().view(np.uint64)
         fl = None if self.flags is None else self.flags.cpu().numpy().view(np.uint64)
+        ls = None if self.seqlens is None else self.seqlens.cpu().tolist()
         return route_counts(mw, self.cfg.S, self.cfg.S, self.cfg.tile_m, self.cfg.tile_n,
-                            self.cfg.tiles_per_bit, self.cfg.causal, fl)
+                            self.cfg.tiles_per_bit, self.cfg.causal, fl, ls, ls)
 
 
 def time_attn(torch, pipe, iters, warmup):
@@ -417,6 +438,20 @@ def main():
             "roofline_frac": round(tr / float(np.median(ts)), 4),
             "t_roof_ms": round(tr * 1e3, 4),
             "frac_16bit_elements": round(cc["n16"] / cc["nvalid"], 4)}
+        del sp
+        # a variable-length batch in the same padded tensors: 16384 and 6000
+        # tokens
+        lens = (16384, 6000)
+        sp = Pipeline(L, sc, qd, kd, vd, torch, seqlens=lens)
+        sp.prep()
+        ts = time_attn(torch, sp, iters=5, warmup=1)
+        cc = sp.counts()
+        tr = roofline_time(cc, sc.D)
+        sweep["i8_f25_varlen_16384_6000"] = {
+            "attn_ms": round(float(np.median(ts)) * 1e3, 4),
+            "tflops": round(algorithmic_flops(cc, sc.D) / float(np.median(ts)) / 1e12, 1),
+            "roofline_frac": round(tr / float(np.median(ts)), 4),
+            "t_roof_ms": round(tr * 1e3, 4)}
         del sp
         result["sweep_c5_attention"] = sweep
         log(f"[bench] sweep {json.dumps(sweep)}")

@@ -103,7 +103,10 @@ void attn_fwd_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char sv1[SH::V_BYTES];
 
   // ---- workgroup -> (b, h, qt): XCD-contiguous chunks of the logical order
-  //      (b, kv-head group) major, query tile descending, head minor ----
+  //      (kv-head group, b) major, query tile descending, head minor.  The
+  //      batch index varies fastest among the groups so that the sequences of
+  //      a variable-length batch spread over the XCDs instead of loading some
+  //      with the long ones. ----
   const int nblk = (int)gridDim.x, bid = (int)blockIdx.x;
   const int xcd = bid & 7, slot = bid >> 3, qn = nblk >> 3, rn = nblk & 7;
   const int lin = xcd * qn + min(xcd, rn) + slot;
@@ -112,7 +115,7 @@ void attn_fwd_kernel(const AttnArgs a) {
   const int rem = lin - grp * per_group;
   const int qt = a.n_qt - 1 - rem / a.heads_per_group;
   const int hh = rem % a.heads_per_group;
-  const int b = grp / a.Hkv, kvh = grp % a.Hkv;
+  const int kvh = grp / a.B, b = grp % a.B;
   const int h = kvh * a.heads_per_group + hh;
 
   // lengths of this batch entry's sequence (a variable-length batch lives in

@@ -245,6 +245,19 @@ def test_bench_route_counts_match_oracle():
         c = bench.route_counts(P.mask_words, S_q, S_k, tm, 64, G, causal)
         ref = A.route_counts(P)
         assert (c["n8"], c["n16"], c["nvalid"], c["nflag"]) == (ref["n8"], ref["n16"], ref["nvalid"], 0)
+    # variable-length batches
+    for causal, S_q, S_k, Lq, Lk in [(True, 300, 300, [300, 17, 0], [300, 200, 5]),
+                                     (False, 200, 333, [200, 64], [0, 333])]:
+        rng = np.random.default_rng(S_k)
+        q = rng.standard_normal((len(Lq), 2, S_q, 8))
+        k = rng.standard_normal((len(Lq), 1, S_k, 8))
+        P = A.make_problem(q, k, k, causal=causal, code="i8", tile_m=128, tile_n=64,
+                           tiles_per_bit=2, frac_16bit=0.4, seed=9, seqlens_q=np.array(Lq),
+                           seqlens_k=np.array(Lk))
+        c = bench.route_counts(P.mask_words, S_q, S_k, 128, 64, 2, causal, seqlens_q=Lq,
+                               seqlens_k=Lk)
+        ref = A.route_counts(P)
+        assert (c["n8"], c["n16"], c["nvalid"]) == (ref["n8"], ref["n16"], ref["nvalid"])
     # flagged-element count: sub-blocks of 32 rows x key tiles
     S = 256
     flags = np.zeros((1, 1, S // 32, 1), np.uint64)
