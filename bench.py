@@ -169,6 +169,55 @@ def sustained_mfma_peaks(torch, iters=100000, reps=3):
 
 
 # ---------------------------------------------------------------------------
+# decode over an int8 key/value cache (HBM-bound)
+# ---------------------------------------------------------------------------
+
+HBM_PEAK = 8.0e12    # MI355X HBM3E, bytes/s
+
+
+def decode_measurement(torch, L, iters=20, warmup=3):
+    """One new token per sequence over a 32768-token int8 cache, Qwen3-8B
+    heads (32 query / 8 KV, head dim 128), batch 8; synthetic seeded bf16
+    inputs quantised once.  Algorithmic bytes per launch: the cache codes
+    (2 D bytes per key per KV head) and scales, the query codes and scales,
+    and the 16-bit output."""
+    B, Hq, Hkv, S_q, S_k, D = 8, 32, 8, 1, 32768, 128
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(4242)
+    q = torch.randn((B, Hq, S_q, D), generator=g, device=dev).to(torch.bfloat16)
+    k = torch.randn((B, Hkv, S_k, D), generator=g, device=dev).to(torch.bfloat16)
+    v = torch.randn((B, Hkv, S_k, D), generator=g, device=dev).to(torch.bfloat16)
+    q8, sq = L.lamp_quantize_blocks(q, 64, "i8")
+    k8, sk = L.lamp_quantize_blocks(k, 64, "i8")
+    v8, sv = L.lamp_quantize_blocks(v, 64, "i8")
+    del k, v
+    out = torch.empty((B, Hq, S_q, D), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(L.lamp_decode_workspace_bytes(B, Hkv, S_k, D), dtype=torch.uint8, device=dev)
+    run = lambda: L.lamp_decode_fwd(q8, sq, k8, sk, v8, sv, causal=True, tile_m=64,
+                                    dtype=torch.bfloat16, out=out, workspace=ws)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(iters)]
+    for a, b_ in ev:
+        a.record()
+        run()
+        b_.record()
+    torch.cuda.synchronize()
+    t = float(np.mean([a.elapsed_time(b_) for a, b_ in ev])) * 1e-3
+    n_kt = -(-S_k // 64)
+    nbytes = (2 * B * Hkv * S_k * D + 2 * B * Hkv * n_kt * 4 + B * Hq * S_q * D + B * Hq * 4 +
+              2 * B * Hq * S_q * D)
+    return {"workload": "qwen3_8b_decode_b8_q1_k32768_int8_kv", "batch": B, "q_heads": Hq,
+            "kv_heads": Hkv, "new_tokens": S_q, "cache_tokens": S_k, "head_dim": D,
+            "ms_mean": round(t * 1e3, 4), "algorithmic_bytes": nbytes,
+            "achieved_gbs": round(nbytes / t / 1e9, 1), "peak_gbs": HBM_PEAK / 1e9,
+            "frac_hbm": round(nbytes / t / HBM_PEAK, 4),
+            "workspace_bytes": int(ws.numel())}
+
+
+# ---------------------------------------------------------------------------
 # traffic from the committed rocprofv3 counter summary of this kernel
 # ---------------------------------------------------------------------------
 
@@ -455,6 +504,10 @@ def main():
         del sp
         result["sweep_c5_attention"] = sweep
         log(f"[bench] sweep {json.dumps(sweep)}")
+    if not args.no_sweep:
+        dm = decode_measurement(torch, L)
+        result["decode_int8_kv"] = dm
+        log(f"[bench] decode over an int8 K/V cache: {json.dumps(dm)}")
     if not args.no_cpu:
         log("[bench] timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(cfg, q, k, v, budget_s=args.cpu_budget)

@@ -40,6 +40,7 @@
 #ifndef LAMP_H_
 #define LAMP_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -240,6 +241,58 @@ typedef struct {
 } lamp_attn_params;
 
 lamp_status lamp_attn_fwd(const lamp_attn_params* p, void* stream);
+
+/*
+ * lamp_decode_fwd -- attention of a few new queries over an int8 key/value
+ * cache (decode).
+ *
+ * Source: TileMix page, section 4 "Why It Matters" (INT8 key/value caches for
+ * the decode phase).  Reading taken: the cache holds K and V as int8 codes
+ * with one fp32 scale per block of 64 keys of one (b, kv head), as
+ * lamp_quantize_blocks writes them (block_rows 64); the queries' codes and
+ * scales come from lamp_quantize_blocks (block_rows tile_m).  For query row i
+ * of head h (KV head h / (Hq / Hkv)):
+ *   s_ij = (cq_i . ck_j) * sQ[i / tile_m] * sK[j / 64] * sm,
+ *   O_i  = sum_j softmax_j(s_i) * sV[j / 64] * cv_j,
+ * over valid j: j < S_k, and j <= i + S_k - S_q when causal (S_q <= S_k).
+ * The GPU rounds p * sV to 16 bits for the P V product.
+ *
+ * Supported: D in {64, 128}; LAMP_I8 codes; Hq % Hkv == 0 and
+ * (Hq / Hkv) * S_q <= 32 (the query group of one KV head fits one 32-column
+ * MFMA block); out_dtype LAMP_F16 or LAMP_BF16.
+ *
+ * Pointers (device): q8 [B, Hq, S_q, D], k8 / v8 [B, Hkv, S_k, D] contiguous
+ * 16-byte aligned codes; q_scale [B, Hq, ceil(S_q / tile_m)], k_scale /
+ * v_scale [B, Hkv, ceil(S_k / 64)]; out [B, Hq, S_q, D] 16-bit at element
+ * strides o_str, head dim contiguous; lse optional [B, Hq, S_q] fp32
+ * (natural log).  workspace: caller-owned device
+ * memory of at least lamp_decode_workspace_bytes(B, Hkv, S_k, D) bytes,
+ * 16-byte aligned (split partials; contents on entry do not matter).
+ */
+typedef struct {
+  uint32_t struct_size;     /* = sizeof(lamp_decode_params); ABI guard       */
+  int32_t causal;           /* 0 / 1                                         */
+  float sm_scale;           /* <= 0 selects 1/sqrt(D)                        */
+  int32_t out_dtype;        /* lamp_dtype: LAMP_F16 | LAMP_BF16              */
+  int64_t B, Hq, Hkv, S_q, S_k, D;
+  const void* q8;
+  const float* q_scale;
+  int32_t tile_m;           /* rows per Q scale block                        */
+  const void* k8;
+  const float* k_scale;
+  const void* v8;
+  const float* v_scale;
+  void* out;
+  int64_t o_str[3];         /* (batch, head, row) element strides           */
+  float* lse;               /* optional                                      */
+} lamp_decode_params;
+
+/* Workspace bytes lamp_decode_fwd needs for these sizes (0 if a size is
+ * negative). */
+size_t lamp_decode_workspace_bytes(int64_t B, int64_t Hkv, int64_t S_k, int64_t D);
+
+lamp_status lamp_decode_fwd(const lamp_decode_params* p, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /* Static name of a status code. */
 const char* lamp_status_string(lamp_status s);

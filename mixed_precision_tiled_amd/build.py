@@ -17,7 +17,8 @@ PROBE_SRC = os.path.join(HERE, "probe", "mfma_sustained.hip")
 PROBE_OUT = os.path.join(HERE, "libmfma_probe.so")
 BUILD = os.path.join(HERE, "_build")
 
-SOURCES = ["lamp_api.cpp", "quant_mask.hip", "attn_d64.hip", "attn_d128.hip", "attn_d256.hip"]
+SOURCES = ["lamp_api.cpp", "quant_mask.hip", "attn_d64.hip", "attn_d128.hip", "attn_d256.hip",
+           "decode.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -1,0 +1,248 @@
+// Attention over an int8 key/value cache (decode), gfx950.
+//
+// Source: "TileMix: Mixed-Precision Attention for Faster LLM Prefill",
+// section 4: the method supports INT8 key/value caches, which matter for the
+// decode phase.  The cache holds K and V as int8 codes with one fp32 scale
+// per block of 64 keys (the per-block quantiser's output); the few new
+// queries are quantised the same way, so a logit is the 8-bit path's
+// (cq . ck) * sQ * sK * sm, and the output uses the dequantised values
+// sV * cv.
+//
+// Decode is bound by reading the cache from HBM (2 D bytes per key, once).
+// Split-K over the keys:
+//   * decode_split_kernel: one wave per (b, kv head, split of 512 keys); the
+//     group's queries (heads_per_group x S_q <= 32 columns) are the B operand
+//     of int8 32x32x32 MFMAs (S^T = K8 Q8^T, K8 straight from global memory
+//     into registers, each byte read once); online softmax per column; V
+//     codes are converted to 16 bits into LDS in the prefill kernel's layout
+//     and multiplied as O^T += V^T P^T, with sV folded into P.  Each wave
+//     writes its unnormalised partial (m, l, O) to the caller's workspace;
+//   * decode_merge_kernel: one thread per output element combines the
+//     splits' partials (log-sum-exp merge) and writes O and LSE.
+#include "attn_kernel.h"
+#include "lamp_internal.h"
+
+namespace lamp {
+
+namespace {
+
+constexpr int kTilesPerSplit = kDecodeTilesPerSplit;
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
+  using SH = AttnShape<D, 1>;
+  using SW = AttnSwizzle<D>;
+  __shared__ __attribute__((aligned(1024))) char sv[SH::V_BYTES];   // one V tile, 16-bit
+
+  const int split = (int)(blockIdx.x % (unsigned)a.n_split);
+  const int grp = (int)(blockIdx.x / (unsigned)a.n_split);          // b * Hkv + kvh
+  const int b = grp / a.Hkv, kvh = grp % a.Hkv;
+  const int lane = threadIdx.x, lr = lane & 31, hf = lane >> 5;
+
+  // column of this lane: query row i of head hh of the KV group
+  const bool col_live = lr < a.cols;
+  const int cc = col_live ? lr : 0;
+  const int hh = cc / a.S_q, i = cc % a.S_q;
+  const int h = kvh * a.hpg + hh;
+  const uint8_t* q8p = a.q8 + (((int64_t)b * a.Hq + h) * a.S_q + i) * D;
+  u32x4 q8[SH::NQ8];
+#pragma unroll
+  for (int t = 0; t < SH::NQ8; ++t) q8[t] = ld_global16(q8p + 32 * t + 16 * hf);
+  const float sQ = a.q_scale[((int64_t)b * a.Hq + h) * a.n_qt + i / a.tile_m];
+  // largest key this column may see (-1: a padding column)
+  const int key_lim = !col_live ? -1 : (a.causal ? min(i + a.S_k - a.S_q, a.S_k - 1) : a.S_k - 1);
+
+  const uint8_t* k8base = a.k8 + (int64_t)grp * a.S_k * D;
+  const uint8_t* v8base = a.v8 + (int64_t)grp * a.S_k * D;
+  const float* sKp = a.k_scale + (int64_t)grp * a.n_kt;
+  const float* sVp = a.v_scale + (int64_t)grp * a.n_kt;
+
+  // V read offsets (transposing reads), as in the prefill kernel
+  int av[SH::ND];
+  {
+    const int sl = lane & 15, g1 = (lane >> 4) & 1;
+    const int svz = SW::v(4 * hf + (sl >> 2));
+#pragma unroll
+    for (int db = 0; db < SH::ND; ++db) {
+      const int lc = 4 * db + 2 * g1 + ((sl & 3) >> 1);
+      av[db] = (4 * hf + (sl >> 2)) * SH::RB16 + ((lc ^ svz) << 4) + 8 * (sl & 1);
+    }
+  }
+  auto kofs = [](int e) { return (e >> 4) * 32 + ((e & 15) >> 2) * 8 + (e & 3); };
+
+  f32x16 O[SH::ND];
+#pragma unroll
+  for (int db = 0; db < SH::ND; ++db) O[db] = f32x16{};
+  float m_run = kNegInf, l_run = 0.f;
+  const float c_log = a.sm_scale * kLog2e * sQ;
+
+  const int kt0 = split * kTilesPerSplit, kt1 = min(a.n_kt, kt0 + kTilesPerSplit);
+  for (int kt = kt0; kt < kt1; ++kt) {
+    const int key0 = kt * SH::TN;
+    // K codes, A operand: rows key0 + 32 kb + lr (clamped; masked below)
+    u32x4 kf0[SH::NQ8], kf1[SH::NQ8];
+    {
+      const uint8_t* p0 = k8base + (int64_t)min(key0 + lr, a.S_k - 1) * D + 16 * hf;
+      const uint8_t* p1 = k8base + (int64_t)min(key0 + 32 + lr, a.S_k - 1) * D + 16 * hf;
+#pragma unroll
+      for (int t = 0; t < SH::NQ8; ++t) {
+        kf0[t] = ld_global16(p0 + 32 * t);
+        kf1[t] = ld_global16(p1 + 32 * t);
+      }
+    }
+    // V codes: one key row per lane
+    u32x4 vcode[D / 16];
+    {
+      const uint8_t* pv = v8base + (int64_t)min(key0 + lane, a.S_k - 1) * D;
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) vcode[c] = ld_global16(pv + 16 * c);
+    }
+    const float sK = ld_uniform(sKp + kt), sV = ld_uniform(sVp + kt);
+
+    // logits (base 2) of the 64 keys x 32 columns
+    i32x16 acc0 = i32x16{}, acc1 = i32x16{};
+#pragma unroll
+    for (int t = 0; t < SH::NQ8; ++t) {
+      acc0 = mfma_i8(kf0[t], q8[t], acc0);
+      acc1 = mfma_i8(kf1[t], q8[t], acc1);
+    }
+    const float c = c_log * sK;
+    const int lim_rel = key_lim - key0 - 4 * hf;
+    float x[32];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int v0 = acc0[e], v1 = acc1[e];
+      x[e] = kofs(e) <= lim_rel ? (float)v0 * c : kNegInf;
+      x[16 + e] = kofs(16 + e) <= lim_rel ? (float)v1 * c : kNegInf;
+    }
+    // online softmax with the exact running maximum
+    float mx = x[0];
+#pragma unroll
+    for (int e = 1; e < 32; ++e) mx = fmaxf(mx, x[e]);
+    mx = halves_max(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float msub = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = m_run == kNegInf ? 0.f : exp2_fast(m_run - m_new);
+    float psum = 0.f;
+    uint32_t pk[16];
+#pragma unroll
+    for (int e = 0; e < 32; e += 2) {
+      const float p0 = exp2_fast(x[e] - msub), p1 = exp2_fast(x[e + 1] - msub);
+      psum += p0 + p1;
+      pk[e >> 1] = pack16x2<BF16>(p0 * sV, p1 * sV);     // the V scale rides on P
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < SH::ND; ++db) O[db] *= alpha;
+
+    // V codes -> 16-bit into LDS: row = key, logical 16-byte chunk lc at
+    // position lc ^ swz(row) (the prefill kernel's V layout)
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t word = vcode[c][2 * half + (j >> 1)];
+          const int sh = 16 * (j & 1);
+          const float f0 = (float)(int)(int8_t)(uint8_t)(word >> sh);
+          const float f1 = (float)(int)(int8_t)(uint8_t)(word >> (sh + 8));
+          w[j] = pack16x2<BF16>(f0, f1);
+        }
+        const int lc = 2 * c + half;
+        st_lds16(sv + lane * SH::RB16 + ((lc ^ SW::v(lane)) << 4), u32x4{w[0], w[1], w[2], w[3]});
+      }
+    }
+    // O^T += V^T P^T (LDS accesses of one wave complete in order)
+#pragma unroll
+    for (int kb_ = 0; kb_ < 2; ++kb_) {
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const int i0 = kb_ * 8 + 4 * c2;
+        const u32x4 pb = {pk[i0], pk[i0 + 1], pk[i0 + 2], pk[i0 + 3]};
+        const char* vrow = sv + (32 * kb_ + 16 * c2) * SH::RB16;
+#pragma unroll
+        for (int db = 0; db < SH::ND; ++db) {
+          const u32x2 lo = ld_lds_tr16(vrow + av[db]);
+          const u32x2 hi = ld_lds_tr16(vrow + 8 * SH::RB16 + av[db]);
+          O[db] = mfma16<BF16>(u32x4{lo.x, lo.y, hi.x, hi.y}, pb, O[db]);
+        }
+      }
+    }
+  }
+
+  // partial of this split: O^T block db holds rows d = 32 db + 8 (r / 4) +
+  // 4 hf + r % 4 of column lr
+  const float l_tot = halves_sum(l_run);
+  const int64_t slot = ((int64_t)grp * a.n_split + split) * 32 + lr;
+  float* wo = a.ws_o + slot * D;
+#pragma unroll
+  for (int db = 0; db < SH::ND; ++db) {
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int d0 = db * 32 + ii * 8 + hf * 4;
+      *reinterpret_cast<f32x4*>(wo + d0) =
+          f32x4{O[db][4 * ii], O[db][4 * ii + 1], O[db][4 * ii + 2], O[db][4 * ii + 3]};
+    }
+  }
+  if (hf == 0) *reinterpret_cast<f32x2*>(a.ws_ml + 2 * slot) = f32x2{m_run, l_tot};
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)a.B * a.Hkv * a.cols * a.D;
+  if (t >= total) return;
+  const int d = (int)(t % a.D);
+  const int col = (int)((t / a.D) % a.cols);
+  const int grp = (int)(t / ((int64_t)a.D * a.cols));
+  const int b = grp / a.Hkv, kvh = grp % a.Hkv;
+  const int hh = col / a.S_q, i = col % a.S_q;
+  const int h = kvh * a.hpg + hh;
+  const int64_t base = (int64_t)grp * a.n_split * 32 + col;
+  float M = kNegInf;
+  for (int s = 0; s < a.n_split; ++s) {
+    const f32x2 ml = *reinterpret_cast<const f32x2*>(a.ws_ml + 2 * (base + (int64_t)s * 32));
+    if (ml.y > 0.f) M = fmaxf(M, ml.x);
+  }
+  float L = 0.f, acc = 0.f;
+  for (int s = 0; s < a.n_split; ++s) {
+    const int64_t slot = base + (int64_t)s * 32;
+    const f32x2 ml = *reinterpret_cast<const f32x2*>(a.ws_ml + 2 * slot);
+    if (ml.y > 0.f) {
+      const float wgt = exp2_fast(ml.x - M);
+      L += ml.y * wgt;
+      acc += a.ws_o[slot * a.D + d] * wgt;
+    }
+  }
+  const float o = L > 0.f ? acc / L : 0.f;
+  uint16_t* op = reinterpret_cast<uint16_t*>(a.out) +
+                 (b * a.o_sb + h * a.o_sh + (int64_t)i * a.o_ss + d);
+  *op = (uint16_t)(pack16x2<BF16>(o, 0.f) & 0xFFFFu);
+  if (d == 0 && a.lse != nullptr)
+    a.lse[((int64_t)b * a.Hq + h) * a.S_q + i] =
+        L > 0.f ? (M + __builtin_amdgcn_logf(L)) * kLn2 : kNegInf;
+}
+
+template <int D, bool BF16>
+hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((decode_split_kernel<D, BF16>),
+                     dim3((unsigned)((int64_t)a.B * a.Hkv * a.n_split)), dim3(64), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t total = (int64_t)a.B * a.Hkv * a.cols * a.D;
+  hipLaunchKernelGGL((decode_merge_kernel<BF16>), dim3((unsigned)((total + 255) / 256)), dim3(256),
+                     0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
+  if (a.D == 64) return a.bf16 ? launch_decode_t<64, true>(a, s) : launch_decode_t<64, false>(a, s);
+  return a.bf16 ? launch_decode_t<128, true>(a, s) : launch_decode_t<128, false>(a, s);
+}
+
+}  // namespace lamp

@@ -303,3 +303,79 @@ lamp_status lamp_attn_fwd(const lamp_attn_params* p, void* stream) {
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// decode over an int8 key/value cache
+// ---------------------------------------------------------------------------
+
+size_t lamp_decode_workspace_bytes(int64_t B, int64_t Hkv, int64_t S_k, int64_t D) {
+  if (B < 0 || Hkv < 0 || S_k < 0 || D < 0) return 0;
+  const int64_t n_split = cdiv(cdiv(S_k, 64), lamp::kDecodeTilesPerSplit);
+  return (size_t)(B * Hkv * n_split * 32 * (D + 2) * (int64_t)sizeof(float));
+}
+
+lamp_status lamp_decode_fwd(const lamp_decode_params* p, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (!p) return fail(LAMP_ERR_NULL, "params is NULL");
+  if (p->struct_size != sizeof(lamp_decode_params))
+    return fail(LAMP_ERR_UNSUPPORTED, "struct_size %u != %zu (ABI mismatch)", p->struct_size,
+                sizeof(lamp_decode_params));
+  if (p->B < 0 || p->Hq < 0 || p->Hkv < 0 || p->S_q < 0 || p->S_k < 0 || p->D < 0)
+    return fail(LAMP_ERR_SHAPE, "negative size");
+  if (p->causal != 0 && p->causal != 1) return fail(LAMP_ERR_SHAPE, "causal must be 0 or 1");
+  if (p->D != 64 && p->D != 128) return fail(LAMP_ERR_UNSUPPORTED, "decode supports D in {64,128}");
+  if (!is16(p->out_dtype)) return fail(LAMP_ERR_UNSUPPORTED, "out_dtype must be LAMP_F16 or LAMP_BF16");
+  if (p->Hkv == 0 || p->Hq % p->Hkv) return fail(LAMP_ERR_UNSUPPORTED, "Hq must be a multiple of Hkv >= 1");
+  if ((p->Hq / p->Hkv) * p->S_q > 32)
+    return fail(LAMP_ERR_UNSUPPORTED, "(Hq/Hkv) * S_q = %lld > 32", (long long)((p->Hq / p->Hkv) * p->S_q));
+  if (p->tile_m < 1) return fail(LAMP_ERR_SHAPE, "tile_m must be positive");
+  if (p->causal && p->S_q > p->S_k) return fail(LAMP_ERR_UNSUPPORTED, "causal needs S_q <= S_k");
+  if (p->S_k > kMaxSeq) return fail(LAMP_ERR_UNSUPPORTED, "S_k above %lld", (long long)kMaxSeq);
+  if (p->B == 0 || p->Hq == 0 || p->S_q == 0) return ok();
+  if (p->S_k == 0) return fail(LAMP_ERR_SHAPE, "S_k == 0 with queries");
+  if (!p->q8 || !p->q_scale || !p->k8 || !p->k_scale || !p->v8 || !p->v_scale || !p->out || !workspace)
+    return fail(LAMP_ERR_NULL, "q8, k8, v8, their scales, out and workspace are required");
+  if (!aligned16(p->q8) || !aligned16(p->k8) || !aligned16(p->v8) || !aligned16(workspace))
+    return fail(LAMP_ERR_ALIGN, "codes and workspace need 16-byte alignment");
+  if (((reinterpret_cast<uintptr_t>(p->out)) & 1u) ||
+      ((reinterpret_cast<uintptr_t>(p->q_scale) | reinterpret_cast<uintptr_t>(p->k_scale) |
+        reinterpret_cast<uintptr_t>(p->v_scale) | reinterpret_cast<uintptr_t>(p->lse)) & 3u))
+    return fail(LAMP_ERR_ALIGN, "out, scales and lse need their element alignment");
+  for (int i = 0; i < 3; ++i)
+    if (p->o_str[i] < 0) return fail(LAMP_ERR_SHAPE, "negative output stride");
+  const size_t need = lamp_decode_workspace_bytes(p->B, p->Hkv, p->S_k, p->D);
+  if (workspace_bytes < need)
+    return fail(LAMP_ERR_SHAPE, "workspace %zu bytes < %zu", workspace_bytes, need);
+  lamp::DecodeArgs a{};
+  a.q8 = static_cast<const uint8_t*>(p->q8);
+  a.q_scale = p->q_scale;
+  a.k8 = static_cast<const uint8_t*>(p->k8);
+  a.k_scale = p->k_scale;
+  a.v8 = static_cast<const uint8_t*>(p->v8);
+  a.v_scale = p->v_scale;
+  a.out = p->out;
+  a.lse = p->lse;
+  a.B = (int32_t)p->B;
+  a.Hq = (int32_t)p->Hq;
+  a.Hkv = (int32_t)p->Hkv;
+  a.S_q = (int32_t)p->S_q;
+  a.S_k = (int32_t)p->S_k;
+  a.D = (int32_t)p->D;
+  a.hpg = (int32_t)(p->Hq / p->Hkv);
+  a.cols = a.hpg * a.S_q;
+  a.tile_m = p->tile_m;
+  a.n_qt = (int32_t)cdiv(p->S_q, p->tile_m);
+  a.n_kt = (int32_t)cdiv(p->S_k, 64);
+  a.n_split = (int32_t)cdiv(a.n_kt, lamp::kDecodeTilesPerSplit);
+  if ((int64_t)a.B * a.Hkv * a.n_split > kMaxGrid) return fail(LAMP_ERR_UNSUPPORTED, "grid too large");
+  a.o_sb = p->o_str[0];
+  a.o_sh = p->o_str[1];
+  a.o_ss = p->o_str[2];
+  a.causal = p->causal;
+  a.sm_scale = p->sm_scale > 0.f ? p->sm_scale : (float)(1.0 / std::sqrt((double)p->D));
+  a.bf16 = p->out_dtype == LAMP_BF16;
+  const int64_t nslot = (int64_t)a.B * a.Hkv * a.n_split * 32;
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_ml = a.ws_o + nslot * a.D;
+  return hip_status(lamp::launch_decode(a, static_cast<hipStream_t>(stream)), "decode launch");
+}

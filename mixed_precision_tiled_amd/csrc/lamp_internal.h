@@ -68,6 +68,29 @@ struct AttnArgs {
   float tau;
 };
 
+// Decode over an int8 key/value cache: 64-key tiles per split of the keys
+constexpr int kDecodeTilesPerSplit = 8;
+
+struct DecodeArgs {
+  const uint8_t* q8;
+  const float* q_scale;        // [B, Hq, n_qt]
+  const uint8_t* k8;
+  const float* k_scale;        // [B, Hkv, n_kt]
+  const uint8_t* v8;
+  const float* v_scale;        // [B, Hkv, n_kt]
+  void* out;
+  float* lse;
+  float* ws_o;                 // [B*Hkv, n_split, 32, D] partial O
+  float* ws_ml;                // [B*Hkv, n_split, 32, 2] partial (m, l), base 2
+  int64_t o_sb, o_sh, o_ss;
+  int32_t B, Hq, Hkv, S_q, S_k, D;
+  int32_t hpg, cols;           // Hq / Hkv, hpg * S_q (<= 32)
+  int32_t tile_m, n_qt, n_kt, n_split;
+  int32_t causal;
+  float sm_scale;
+  bool bf16;
+};
+
 struct AttnConfig {
   int d;            // 64 | 128 | 256
   int nw;           // waves per workgroup = tile_m / 32
@@ -83,5 +106,6 @@ hipError_t launch_build_mask_template(const TemplateMaskArgs& a, hipStream_t s);
 hipError_t launch_attn_d64(const AttnArgs& a, const AttnConfig& c, hipStream_t s);
 hipError_t launch_attn_d128(const AttnArgs& a, const AttnConfig& c, hipStream_t s);
 hipError_t launch_attn_d256(const AttnArgs& a, const AttnConfig& c, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 
 }  // namespace lamp

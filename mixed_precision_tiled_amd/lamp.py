@@ -236,6 +236,57 @@ def lamp_attn_fwd(q, k, v, q8, k8, q_scale, k_scale, mask, *, code, causal, tile
     return out
 
 
+class lamp_decode_params(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", _u32), ("causal", _i32), ("sm_scale", ctypes.c_float), ("out_dtype", _i32),
+        ("B", _i64), ("Hq", _i64), ("Hkv", _i64), ("S_q", _i64), ("S_k", _i64), ("D", _i64),
+        ("q8", _vp), ("q_scale", _vp), ("tile_m", _i32), ("k8", _vp), ("k_scale", _vp),
+        ("v8", _vp), ("v_scale", _vp), ("out", _vp), ("o_str", _i64 * 3), ("lse", _vp),
+    ]
+
+
+_lib.lamp_decode_workspace_bytes.restype = ctypes.c_size_t
+_lib.lamp_decode_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64]
+_lib.lamp_decode_fwd.restype = _i32
+_lib.lamp_decode_fwd.argtypes = [ctypes.POINTER(lamp_decode_params), _vp, ctypes.c_size_t, _vp]
+
+
+def lamp_decode_workspace_bytes(B, Hkv, S_k, D):
+    return int(_lib.lamp_decode_workspace_bytes(B, Hkv, S_k, D))
+
+
+def lamp_decode_fwd(q8, q_scale, k8, k_scale, v8, v_scale, *, causal, tile_m, dtype,
+                    sm_scale=0.0, out=None, lse=None, workspace=None):
+    """Attention of q8 [B,Hq,S_q,D] over the int8 cache k8/v8 [B,Hkv,S_k,D]
+    (codes and scales from lamp_quantize_blocks; K/V in 64-key blocks).
+    Returns out [B,Hq,S_q,D] of torch dtype `dtype` (float16/bfloat16)."""
+    B, Hq, S_q, D = q8.shape
+    _, Hkv, S_k, _ = k8.shape
+    if dtype not in _DT16:
+        raise TypeError("dtype must be float16 or bfloat16")
+    if out is None:
+        out = torch.empty((B, Hq, S_q, D), dtype=dtype, device=q8.device)
+    need = lamp_decode_workspace_bytes(B, Hkv, S_k, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q8.device)
+    for t in (q8, q_scale, k8, k_scale, v8, v_scale, lse, workspace):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("codes, scales, lse and workspace must be contiguous")
+    p = lamp_decode_params()
+    p.struct_size = ctypes.sizeof(lamp_decode_params)
+    p.causal = int(bool(causal))
+    p.sm_scale = sm_scale
+    p.out_dtype = _DT16[dtype]
+    p.B, p.Hq, p.Hkv, p.S_q, p.S_k, p.D = B, Hq, Hkv, S_q, S_k, D
+    p.q8, p.q_scale, p.tile_m = q8.data_ptr(), q_scale.data_ptr(), tile_m
+    p.k8, p.k_scale, p.v8, p.v_scale = k8.data_ptr(), k_scale.data_ptr(), v8.data_ptr(), v_scale.data_ptr()
+    p.out = out.data_ptr()
+    p.o_str = _strides3(out)
+    p.lse = None if lse is None else lse.data_ptr()
+    _check(_lib.lamp_decode_fwd(ctypes.byref(p), _ptr(workspace), workspace.numel(), _stream(q8)))
+    return out
+
+
 def flags_shape(B, Hq, S_q, S_k, tile_n=64, sub_rows=32):
     return (B, Hq, cdiv(S_q, sub_rows), max(1, cdiv(cdiv(S_k, tile_n), 64)))
 

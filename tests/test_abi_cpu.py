@@ -67,6 +67,59 @@ def test_struct_layout_matches_binding(tmp_path, lamp):
         assert int(out[f]) == getattr(P, f).offset, f
 
 
+def test_decode_struct_layout_matches_binding(tmp_path, lamp):
+    from mixed_precision_tiled_amd.lamp import lamp_decode_params as P
+    fields = [f[0] for f in P._fields_]
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "lamp.h"', "int main(void){",
+             'printf("size %zu\\n", sizeof(lamp_decode_params));']
+    for f in fields:
+        lines.append(f'printf("{f} %zu\\n", offsetof(lamp_decode_params, {f}));')
+    lines.append("return 0;}")
+    c = tmp_path / "dlayout.c"
+    c.write_text("\n".join(lines))
+    exe = tmp_path / "dlayout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(c), "-o", str(exe)],
+                   check=True)
+    out = dict(l.split() for l in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                  check=True).stdout.splitlines())
+    assert int(out["size"]) == ctypes.sizeof(P)
+    for f in fields:
+        assert int(out[f]) == getattr(P, f).offset, f
+
+
+def test_decode_validation(lamp):
+    from mixed_precision_tiled_amd.lamp import lamp_decode_params as P
+    f = _lib(lamp).lamp_decode_fwd
+    ws = ctypes.c_void_p(1 << 20)
+
+    def params(**kw):
+        p = P()
+        p.struct_size = ctypes.sizeof(P)
+        p.causal, p.out_dtype = 1, 1
+        p.B, p.Hq, p.Hkv, p.S_q, p.S_k, p.D = 1, 8, 2, 1, 1000, 128
+        p.q8 = p.q_scale = p.k8 = p.k_scale = p.v8 = p.v_scale = p.out = 4096
+        p.tile_m = 64
+        p.o_str[:] = [8 * 128, 128, 128]
+        for key, val in kw.items():
+            setattr(p, key, val)
+        return p
+    need = lamp.lamp_decode_workspace_bytes(1, 2, 1000, 128)
+    assert need == 1 * 2 * 2 * 32 * 130 * 4
+    cases = [(dict(struct_size=4), 3), (dict(D=256), 3), (dict(out_dtype=2), 3), (dict(Hkv=3), 3),
+             (dict(S_q=9), 3),                   # 4 heads x 9 rows > 32 columns
+             (dict(causal=2), 2), (dict(S_q=2, S_k=1), 3), (dict(tile_m=0), 2),
+             (dict(k8=None), 1), (dict(q8=4100), 4), (dict(out=4097), 4), (dict(B=-1), 2),
+             (dict(B=0), 0), (dict(S_k=0, causal=0), 2)]
+    for kw, st in cases:
+        p = params(**kw)
+        assert f(ctypes.byref(p), ws, need, None) == st, kw
+    p = params()
+    assert f(ctypes.byref(p), ws, need - 1, None) == 2            # workspace too small
+    assert f(ctypes.byref(p), None, need, None) == 1
+    assert f(ctypes.byref(p), ctypes.c_void_p((1 << 20) + 8), need, None) == 4
+    assert f(None, ws, need, None) == 1
+
+
 def test_library_exports_every_declared_symbol(lamp):
     names = declared_functions()
     assert set(names) >= {"lamp_quantize_blocks", "lamp_build_mask", "lamp_attn_fwd",

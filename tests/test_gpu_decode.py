@@ -1,0 +1,80 @@
+"""GPU parity of lamp_decode_fwd (attention over an int8 key/value cache)
+against oracle.decode, element by element."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import compare, decode
+
+pytestmark = pytest.mark.gpu
+
+
+def L():
+    import mixed_precision_tiled_amd as m
+    return m
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def rand16(shape, seed, dtype):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(*shape, generator=g).to(dtype)
+
+
+DT = {"bf16": torch.bfloat16, "f16": torch.float16}
+
+CASES = [
+    # D, dtype, B, Hq, Hkv, S_q, S_k, causal, tile_m
+    (128, "bf16", 2, 32, 8, 1, 5000, True, 64),      # one new token, Qwen3-8B-like heads
+    (128, "bf16", 1, 8, 2, 4, 777, True, 64),        # a few new tokens, ragged cache
+    (64, "f16", 2, 4, 4, 8, 300, False, 64),
+    (128, "bf16", 1, 4, 1, 8, 64, True, 128),        # 32 columns, one tile
+    (128, "f16", 1, 2, 2, 3, 1, False, 64),          # a one-key cache
+    (64, "bf16", 3, 16, 2, 2, 4097, True, 64),       # more than one split, ragged last split
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "d{}_{}_b{}_h{}x{}_q{}_k{}_{}".format(
+    c[0], c[1], c[2], c[3], c[4], c[5], c[6], "causal" if c[7] else "full"))
+def test_decode_parity(case):
+    D, dt, B, Hq, Hkv, S_q, S_k, causal, tm = case
+    print(f"[decode] {case}", flush=True)
+    q = rand16((B, Hq, S_q, D), 1, DT[dt])
+    k = rand16((B, Hkv, S_k, D), 2, DT[dt])
+    v = rand16((B, Hkv, S_k, D), 3, DT[dt])
+    qd, kd, vd = q.to(dev()), k.to(dev()), v.to(dev())
+    q8, sq = L().lamp_quantize_blocks(qd, tm, "i8")
+    k8, sk = L().lamp_quantize_blocks(kd, 64, "i8")
+    v8, sv = L().lamp_quantize_blocks(vd, 64, "i8")
+    lse = torch.full((B, Hq, S_q), float("nan"), device=dev())
+    out = L().lamp_decode_fwd(q8, sq, k8, sk, v8, sv, causal=causal, tile_m=tm, dtype=DT[dt],
+                              lse=lse)
+    torch.cuda.synchronize()
+    P, (vc, vs) = decode.decode_problem(q.double().numpy(), k.double().numpy(),
+                                        v.double().numpy(), causal=causal, tile_m=tm)
+    assert (q8.cpu().numpy() == P.q_codes).all() and (k8.cpu().numpy() == P.k_codes).all()
+    assert (v8.cpu().numpy() == vc).all() and (sv.cpu().numpy() == vs).all()
+    got, glse = out.float().cpu().numpy(), lse.cpu().numpy()
+    for b in range(B):
+        for h in range(Hq):
+            O, lse_ref = decode.decode_attention(P, b, h, np.arange(S_q))
+            st = compare.check(got[b, h], O, dt)
+            assert st["ok"], f"({b},{h}): {st}"
+            assert np.abs(glse[b, h] - lse_ref).max() <= 2e-3 + 1e-5 * np.abs(lse_ref).max()
+
+
+def test_decode_workspace_and_errors():
+    m = L()
+    assert m.lamp_decode_workspace_bytes(2, 8, 5000, 128) == 2 * 8 * 10 * 32 * 130 * 4
+    x = torch.zeros((1, 40, 2, 128), dtype=torch.uint8, device=dev())
+    s = torch.zeros((1, 40, 1), dtype=torch.float32, device=dev())
+    kx = torch.zeros((1, 1, 64, 128), dtype=torch.uint8, device=dev())
+    ks = torch.zeros((1, 1, 1), dtype=torch.float32, device=dev())
+    with pytest.raises(m.LampError):          # (Hq / Hkv) * S_q = 80 > 32
+        m.lamp_decode_fwd(x, s, kx, ks, kx, ks, causal=True, tile_m=64, dtype=torch.bfloat16)
+    small = torch.empty(16, dtype=torch.uint8, device=dev())
+    with pytest.raises(m.LampError):          # workspace too small
+        m.lamp_decode_fwd(x[:, :8], s[:, :8], kx, ks, kx, ks, causal=True, tile_m=64,
+                          dtype=torch.bfloat16, workspace=small)
