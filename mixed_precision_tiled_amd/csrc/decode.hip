@@ -17,8 +17,8 @@
 //     codes are converted to 16 bits into LDS in the prefill kernel's layout
 //     and multiplied as O^T += V^T P^T, with sV folded into P.  Each wave
 //     writes its unnormalised partial (m, l, O) to the caller's workspace;
-//   * decode_merge_kernel: one thread per output element combines the
-//     splits' partials (log-sum-exp merge) and writes O and LSE.
+//   * decode_merge_kernel: one workgroup per (b, KV head, column) combines
+//     the splits' partials (log-sum-exp merge) and writes O and LSE.
 #include "attn_kernel.h"
 #include "lamp_internal.h"
 
@@ -27,6 +27,7 @@ namespace lamp {
 namespace {
 
 constexpr int kTilesPerSplit = kDecodeTilesPerSplit;
+constexpr int kMergeThreads = 128;
 
 template <int D, bool BF16>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
@@ -190,38 +191,61 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   if (hf == 0) *reinterpret_cast<f32x2*>(a.ws_ml + 2 * slot) = f32x2{m_run, l_tot};
 }
 
+// One workgroup per (b, KV head, column): the splits' (m, l) go through LDS
+// once, every thread then owns one head-dim element and sums the splits'
+// partial O with independent loads.
 template <bool BF16>
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = (int64_t)a.B * a.Hkv * a.cols * a.D;
-  if (t >= total) return;
-  const int d = (int)(t % a.D);
-  const int col = (int)((t / a.D) % a.cols);
-  const int grp = (int)(t / ((int64_t)a.D * a.cols));
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs a) {
+  __shared__ float wgt[kMergeMaxSplit];
+  __shared__ float red[kMergeThreads / 64];
+  const int col = (int)(blockIdx.x % (unsigned)a.cols);
+  const int grp = (int)(blockIdx.x / (unsigned)a.cols);
   const int b = grp / a.Hkv, kvh = grp % a.Hkv;
   const int hh = col / a.S_q, i = col % a.S_q;
   const int h = kvh * a.hpg + hh;
-  const int64_t base = (int64_t)grp * a.n_split * 32 + col;
+  const int tid = threadIdx.x;
+  const int64_t base = (int64_t)grp * a.n_split * 32 + col;     // slot of split 0
+  // maximum of the splits' m over splits that saw a key (l > 0)
   float M = kNegInf;
-  for (int s = 0; s < a.n_split; ++s) {
+  for (int s = tid; s < a.n_split; s += kMergeThreads) {
     const f32x2 ml = *reinterpret_cast<const f32x2*>(a.ws_ml + 2 * (base + (int64_t)s * 32));
     if (ml.y > 0.f) M = fmaxf(M, ml.x);
   }
-  float L = 0.f, acc = 0.f;
-  for (int s = 0; s < a.n_split; ++s) {
-    const int64_t slot = base + (int64_t)s * 32;
-    const f32x2 ml = *reinterpret_cast<const f32x2*>(a.ws_ml + 2 * slot);
-    if (ml.y > 0.f) {
-      const float wgt = exp2_fast(ml.x - M);
-      L += ml.y * wgt;
-      acc += a.ws_o[slot * a.D + d] * wgt;
-    }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  if ((tid & 63) == 0) red[tid >> 6] = M;
+  __syncthreads();
+  M = red[0];
+#pragma unroll
+  for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, red[w]);
+  __syncthreads();
+  // split weights 2^(m - M) (0 for splits without keys) and L
+  float Lp = 0.f;
+  for (int s = tid; s < a.n_split; s += kMergeThreads) {
+    const f32x2 ml = *reinterpret_cast<const f32x2*>(a.ws_ml + 2 * (base + (int64_t)s * 32));
+    const float w = ml.y > 0.f ? exp2_fast(ml.x - M) : 0.f;
+    wgt[s] = w;
+    Lp += ml.y * w;
   }
-  const float o = L > 0.f ? acc / L : 0.f;
-  uint16_t* op = reinterpret_cast<uint16_t*>(a.out) +
-                 (b * a.o_sb + h * a.o_sh + (int64_t)i * a.o_ss + d);
-  *op = (uint16_t)(pack16x2<BF16>(o, 0.f) & 0xFFFFu);
-  if (d == 0 && a.lse != nullptr)
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) Lp += __shfl_xor(Lp, off, 64);
+  if ((tid & 63) == 0) red[tid >> 6] = Lp;
+  __syncthreads();
+  float L = 0.f;
+#pragma unroll
+  for (int w = 0; w < kMergeThreads / 64; ++w) L += red[w];
+  // O = sum_s w_s O_s / L, one head-dim element per thread
+  for (int d = tid; d < a.D; d += kMergeThreads) {
+    float acc = 0.f;
+    const float* po = a.ws_o + base * a.D + d;
+#pragma unroll 8
+    for (int s = 0; s < a.n_split; ++s) acc += po[(int64_t)s * 32 * a.D] * wgt[s];
+    const float o = L > 0.f ? acc / L : 0.f;
+    uint16_t* op = reinterpret_cast<uint16_t*>(a.out) +
+                   (b * a.o_sb + h * a.o_sh + (int64_t)i * a.o_ss + d);
+    *op = (uint16_t)(pack16x2<BF16>(o, 0.f) & 0xFFFFu);
+  }
+  if (tid == 0 && a.lse != nullptr)
     a.lse[((int64_t)b * a.Hq + h) * a.S_q + i] =
         L > 0.f ? (M + __builtin_amdgcn_logf(L)) * kLn2 : kNegInf;
 }
@@ -232,9 +256,8 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
                      dim3((unsigned)((int64_t)a.B * a.Hkv * a.n_split)), dim3(64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t total = (int64_t)a.B * a.Hkv * a.cols * a.D;
-  hipLaunchKernelGGL((decode_merge_kernel<BF16>), dim3((unsigned)((total + 255) / 256)), dim3(256),
-                     0, s, a);
+  hipLaunchKernelGGL((decode_merge_kernel<BF16>), dim3((unsigned)((int64_t)a.B * a.Hkv * a.cols)),
+                     dim3(kMergeThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -367,7 +367,8 @@ lamp_status lamp_decode_fwd(const lamp_decode_params* p, void* workspace, size_t
   a.n_qt = (int32_t)cdiv(p->S_q, p->tile_m);
   a.n_kt = (int32_t)cdiv(p->S_k, 64);
   a.n_split = (int32_t)cdiv(a.n_kt, lamp::kDecodeTilesPerSplit);
-  if ((int64_t)a.B * a.Hkv * a.n_split > kMaxGrid) return fail(LAMP_ERR_UNSUPPORTED, "grid too large");
+  if ((int64_t)a.B * a.Hkv * a.n_split > kMaxGrid || a.n_split > lamp::kMergeMaxSplit)
+    return fail(LAMP_ERR_UNSUPPORTED, "grid too large");
   a.o_sb = p->o_str[0];
   a.o_sh = p->o_str[1];
   a.o_ss = p->o_str[2];

@@ -70,6 +70,7 @@ struct AttnArgs {
 
 // Decode over an int8 key/value cache: 64-key tiles per split of the keys
 constexpr int kDecodeTilesPerSplit = 8;
+constexpr int kMergeMaxSplit = 4096;     // splits of one merge (S_k <= 2^20 / 512 keys)
 
 struct DecodeArgs {
   const uint8_t* q8;
