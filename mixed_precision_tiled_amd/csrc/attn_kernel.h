@@ -20,10 +20,13 @@
 //     cross-half exchange, and alpha rescales only the lane's own rows;
 //   * P V is computed as O^T = V^T P^T: the S^T accumulator registers are, once
 //     converted to 16 bits, exactly the B operand of the next MFMA (no LDS
-//     round trip for P); V is staged in LDS transposed (d-major) with the key
-//     order inside each 16-key group permuted to match that register layout;
+//     round trip for P); V stays key-major in LDS and is read with the
+//     transposing ds_read_b64_tr_b16, the key order inside each 16-key group
+//     permuted to match that register layout;
 //   * K (as K16 or K8, whichever the mask selects) and V are double-buffered
-//     in LDS through registers, one barrier per key tile;
+//     in LDS through direct-to-LDS buffer loads, one barrier per key tile; a
+//     step computes the logits of tile kt and interleaves P V of tile kt-1
+//     with the softmax arithmetic of tile kt;
 //   * workgroups are mapped so that each XCD processes whole KV-head groups
 //     (shared K/V in its L2), longest causal query tiles first.
 #pragma once
