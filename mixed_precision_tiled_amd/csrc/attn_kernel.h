@@ -473,7 +473,7 @@ void attn_fwd_kernel(const AttnArgs a) {
     for (int e = 1; e < 32; ++e) mx = fmaxf(mx, x[e]);
     mx = (mx - xoff) * cm;
     mx = halves_max(mx);
-    // the weights overwrite x in place
+    // the 16-bit weights go to pk (the fp32 weights overwrite x in place)
     auto weights = [&](float mref) {
       if constexpr (LAZY) {
         // exp2((x - xoff) * cm - m) with the offset folded into the constant
@@ -483,18 +483,22 @@ void attn_fwd_kernel(const AttnArgs a) {
       } else {
         const float msub = (mref == kNegInf) ? 0.f : mref;
         if (EXP8 && !lg.is16) {
-          // x = s - m rounded to e4m3, exp, rounded to e4m3 again
+          // x = s - m rounded to e4m3, exp, rounded to e4m3 again; four
+          // values per code word, the final codes converted straight to the
+          // 16-bit P operand
 #pragma unroll
-          for (int e = 0; e < 32; e += 2) {
-            const float x0 = fmaxf(__builtin_fmaf(x[e], cm, -msub), -448.f);
-            const float x1 = fmaxf(__builtin_fmaf(x[e + 1], cm, -msub), -448.f);
-            const f32x2 xq = e4m3x2_to_f32(f32x2_to_e4m3(x0, x1));
-            const float e0 = exp2_fast(xq.x * kLog2e);
-            const float e1 = exp2_fast(xq.y * kLog2e);
-            const f32x2 pq = e4m3x2_to_f32(f32x2_to_e4m3(e0, e1));
-            x[e] = pq.x;
-            x[e + 1] = pq.y;
+          for (int e = 0; e < 32; e += 4) {
+            float xs[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) xs[j] = fmaxf(__builtin_fmaf(x[e + j], cm, -msub), -448.f);
+            const uint32_t xc = f32x4_to_e4m3(xs[0], xs[1], xs[2], xs[3]);
+            const f32x2 xlo = e4m3x2_to_f32<false>(xc), xhi = e4m3x2_to_f32<true>(xc);
+            const uint32_t pc = f32x4_to_e4m3(exp2_fast(xlo.x * kLog2e), exp2_fast(xlo.y * kLog2e),
+                                              exp2_fast(xhi.x * kLog2e), exp2_fast(xhi.y * kLog2e));
+            pk[e >> 1] = e4m3x2_to_16<BF16, false>(pc);
+            pk[(e >> 1) + 1] = e4m3x2_to_16<BF16, true>(pc);
           }
+          return;
         } else {
           const float c2 = cm * kLog2e, m2 = msub * kLog2e;
 #pragma unroll

@@ -68,15 +68,32 @@ __device__ __forceinline__ f32x16 mfma_e4m3(u32x4 a0, u32x4 a1, u32x4 b0, u32x4 
 // conversions
 // ---------------------------------------------------------------------------
 
-// two fp32 -> two OCP e4m3 codes in the low 16 bits (round-to-nearest-even;
-// callers keep |x| <= 448 so no value saturates or overflows).
-__device__ __forceinline__ uint32_t f32x2_to_e4m3(float a, float b) {
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+// four fp32 -> four OCP e4m3 codes, a in byte 0 .. d in byte 3
+// (round-to-nearest-even; callers keep |x| <= 448 so no value saturates or
+// overflows).  The second conversion writes the upper half of the first's
+// result.
+__device__ __forceinline__ uint32_t f32x4_to_e4m3(float a, float b, float c, float d) {
+  // the high half of the first word is overwritten by the second conversion,
+  // so any dead value serves as its old contents (saves a register clear)
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, a), false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
-// e4m3 code pair (low 16 bits) -> two fp32 (exact)
+// e4m3 codes in bytes 2 HI, 2 HI + 1 -> two fp32 (exact)
+template <bool HI>
 __device__ __forceinline__ f32x2 e4m3x2_to_f32(uint32_t codes) {
-  return __builtin_amdgcn_cvt_pk_f32_fp8((int)codes, false);
+  return __builtin_amdgcn_cvt_pk_f32_fp8((int)codes, HI);
+}
+
+// e4m3 codes in bytes 2 HI, 2 HI + 1 -> two packed 16-bit values (exact:
+// every e4m3 value is a bf16 and an fp16 value; scale 1)
+template <bool BF16, bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_16(uint32_t codes) {
+  if constexpr (BF16) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)codes, 1.f, HI));
+  } else {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)codes, 1.f, HI));
+  }
 }
 
 template <bool BF16>

@@ -85,8 +85,8 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantArgs a) {
       } else if constexpr (E4M3) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) y[e] = fminf(fmaxf(y[e], -448.f), 448.f);
-        packed.x = f32x2_to_e4m3(y[0], y[1]) | (f32x2_to_e4m3(y[2], y[3]) << 16);
-        packed.y = f32x2_to_e4m3(y[4], y[5]) | (f32x2_to_e4m3(y[6], y[7]) << 16);
+        packed.x = f32x4_to_e4m3(y[0], y[1], y[2], y[3]);
+        packed.y = f32x4_to_e4m3(y[4], y[5], y[6], y[7]);
       } else {
         uint32_t w[2] = {0u, 0u};
 #pragma unroll
