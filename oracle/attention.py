@@ -48,6 +48,11 @@ precision; a sub-block is sub_rows query rows by one key tile, flagged when
 some valid 8-bit-routed logit lies within tau of the look-ahead running
 maximum m' = max(m, rowmax of the tile's 8-bit logits); flagged sub-blocks use
 16-bit logits for the whole sub-block.
+
+Optional 8-bit P V (``pv8``, with exp8 and mask routing; a variant the pages
+do not specify): on 8-bit tiles the e4m3 weights multiply V quantised to e4m3
+with one power-of-two scale per tile_n-key block (``quant.quantize_v_tiles``);
+16-bit tiles keep the 16-bit V.  The normaliser still sums the weights.
 """
 from dataclasses import dataclass, field
 
@@ -80,6 +85,9 @@ class Problem:
     sub_rows: int = 32
     seqlens_q: np.ndarray = None  # [B] lengths of a variable-length batch (None: S_q)
     seqlens_k: np.ndarray = None  # [B] (None: S_k)
+    pv8: bool = False             # 8-bit P V on 8-bit tiles (needs exp8, mask routing)
+    v_codes: np.ndarray = None    # [B, Hkv, S_k, D] e4m3 codes of V (pv8)
+    v_scales: np.ndarray = None   # [B, Hkv, n_kt] power-of-two block scales (pv8)
 
     def __post_init__(self):
         B, Hq, S_q, D = self.q.shape
@@ -105,6 +113,12 @@ class Problem:
         self.qv = quant.code_values(self.q_codes, self.code)
         self.kv = quant.code_values(self.k_codes, self.code)
         self.bits = omask.unpack_bits(self.mask_words, self.n_g)   # [B,Hq,n_qt,n_g]
+        if self.pv8:
+            if not self.exp8 or self.adaptive:
+                raise ValueError("the 8-bit P V product needs exp8 and mask routing")
+            if self.v_codes is None or self.v_scales is None:
+                raise ValueError("pv8 needs V codes and scales")
+            self.v8 = quant.dequantize(self.v_codes, self.v_scales, self.tile_n, "e4m3")
 
     def kvh(self, h):
         return h // (self.Hq // self.Hkv)
@@ -132,6 +146,8 @@ def make_problem(q, k, v, *, causal, code, tile_m, tile_n, tiles_per_bit, frac_1
     v = np.asarray(v, dtype=np.float64)
     qc, qs = quant.quantize_blocks(q, tile_m, code, kw.get("seqlens_q"))
     kc, ks = quant.quantize_blocks(k, tile_n, code, kw.get("seqlens_k"))
+    if kw.get("pv8") and "v_codes" not in kw:
+        kw["v_codes"], kw["v_scales"] = quant.quantize_v_tiles(v, tile_n, kw.get("seqlens_k"))
     B, Hq, S_q, _ = q.shape
     S_k = k.shape[2]
     if mask_words is None:
@@ -337,7 +353,12 @@ def attn_lamp(P, b, h, sub_blocks):
             alpha = np.where(np.isfinite(m), np.exp(m - m_new), 0.0)
         alpha = np.where(np.isfinite(m_new), alpha, 1.0)
         l = alpha * l + p.sum(axis=1)
-        acc = alpha[:, None] * acc + p @ vh[cols]
+        if P.pv8:
+            # 8-bit weights meet the e4m3 V codes of their tile (products exact)
+            p8v = np.where(use16, 0.0, p)
+            acc = alpha[:, None] * acc + (p - p8v) @ vh[cols] + p8v @ P.v8[b, P.kvh(h)][cols]
+        else:
+            acc = alpha[:, None] * acc + p @ vh[cols]
         m = np.where(np.isfinite(m_new), m_new, m)
         n8 += int((ok & r8).sum())
         n16 += int((ok & ~np.broadcast_to(r8_tiles[qt, kt][:, None], ok.shape)).sum())
