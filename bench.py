@@ -121,6 +121,13 @@ def roofline_time(c, D):
         2.0 * D * c["nvalid"] / PEAK16
 
 
+def roofline_time_pv8(c, D):
+    """Roofline with the 8-bit P V product: P V of 8-bit-routed elements at the
+    8-bit rate too."""
+    return 2.0 * D * c["n8"] / PEAK8 + 2.0 * D * (c["n16"] + c["nflag"]) / PEAK16 + \
+        2.0 * D * c["n8"] / PEAK8 + 2.0 * D * c["n16"] / PEAK16
+
+
 def roofline_time_at(c, D, p8, p16):
     return 2.0 * D * c["n8"] / p8 + 2.0 * D * (c["n16"] + c["nflag"]) / p16 + \
         2.0 * D * c["nvalid"] / p16
@@ -287,8 +294,9 @@ def cpu_baseline(cfg, q, k, v, budget_s=12.0):
 class Pipeline:
     """Preallocated buffers for one configuration; run() enqueues one step."""
 
-    def __init__(self, L, cfg, qd, kd, vd, torch, template=None, seqlens=None):
+    def __init__(self, L, cfg, qd, kd, vd, torch, template=None, seqlens=None, pv8=False):
         self.L, self.cfg, self.torch = L, cfg, torch
+        self.pv8 = pv8                 # 8-bit P V on 8-bit tiles (V quantised too)
         self.template = template       # (sink, band, stride) groups, or the random mask
         # variable-length batch: one length per sequence (queries = keys)
         self.seqlens = None if seqlens is None else \
@@ -306,6 +314,10 @@ class Pipeline:
         if cfg.adaptive:
             self.flags = torch.empty(L.lamp.flags_shape(B, Hq, S, S), dtype=torch.int64, device=dev)
         self.f16 = 0.0 if cfg.mask_all_ones else cfg.frac_16bit
+        self.v8 = self.vs = None
+        if pv8:
+            self.v8 = torch.empty((B, Hkv, cfg.n_kt, D, 64), dtype=torch.uint8, device=dev)
+            self.vs = torch.empty((B, Hkv, cfg.n_kt), dtype=torch.float32, device=dev)
 
     def prep(self):
         L, c = self.L, self.cfg
@@ -313,6 +325,8 @@ class Pipeline:
                                seqlens=self.seqlens)
         L.lamp_quantize_blocks(self.kd, c.tile_n, c.code, codes=self.k8, scales=self.sk,
                                seqlens=self.seqlens)
+        if self.pv8:
+            L.lamp_quantize_v_tiles(self.vd, codes=self.v8, scales=self.vs, seqlens=self.seqlens)
         if self.template is not None:
             L.lamp_build_mask_template(c.B, c.Hq, c.S, c.S, c.tile_m, c.tile_n, c.tiles_per_bit,
                                        *self.template, c.words_per_row, mask=self.mask)
@@ -327,7 +341,8 @@ class Pipeline:
                         tiles_per_bit=c.tiles_per_bit, words_per_row=c.words_per_row,
                         mode=L.LAMP_MODE_ADAPTIVE if c.adaptive else L.LAMP_MODE_MASK,
                         exp8=c.exp8, tau=c.tau, sub_rows=c.sub_rows, out=self.out,
-                        flags_out=self.flags, seqlens_q=self.seqlens, seqlens_k=self.seqlens)
+                        flags_out=self.flags, seqlens_q=self.seqlens, seqlens_k=self.seqlens,
+                        v8=self.v8, v_scale=self.vs)
 
     def counts(self):
         mw = self.mask.cpu().numpy().view(np.uint64)
@@ -502,6 +517,21 @@ def main():
             "roofline_frac": round(tr / float(np.median(ts)), 4),
             "t_roof_ms": round(tr * 1e3, 4)}
         del sp
+        # the 8-bit P V product on 8-bit tiles (e4m3 path with 8-bit
+        # exponentials), all tiles 8-bit and a quarter of the groups 16-bit
+        for f in (0.0, 0.25):
+            sc = get_config("C5", f, "e4m3")
+            sp = Pipeline(L, sc, qd, kd, vd, torch, pv8=True)
+            sp.prep()
+            ts = time_attn(torch, sp, iters=5, warmup=1)
+            cc = sp.counts()
+            tr = roofline_time_pv8(cc, sc.D)
+            sweep[f"e4m3_f{int(round(100 * f)):02d}_pv8"] = {
+                "attn_ms": round(float(np.median(ts)) * 1e3, 4),
+                "tflops": round(algorithmic_flops(cc, sc.D) / float(np.median(ts)) / 1e12, 1),
+                "roofline_frac": round(tr / float(np.median(ts)), 4),
+                "t_roof_ms": round(tr * 1e3, 4)}
+            del sp
         result["sweep_c5_attention"] = sweep
         log(f"[bench] sweep {json.dumps(sweep)}")
     if not args.no_sweep:

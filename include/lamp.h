@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define LAMP_ABI_VERSION 2
+#define LAMP_ABI_VERSION 3
 
 typedef enum {
   LAMP_OK = 0,
@@ -109,6 +109,37 @@ lamp_status lamp_quantize_blocks_varlen(const void* x, int32_t x_dtype, int64_t 
                                         int64_t ss, const int32_t* seqlens, int32_t block_rows,
                                         int32_t code_dtype, void* codes, float* scales,
                                         void* stream);
+
+/*
+ * lamp_quantize_v_tiles -- V as e4m3 codes for the optional 8-bit P V
+ * product (lamp_attn_params.pv8).
+ *
+ * Source: LampAttention abstract (products evaluated in 8-bit formats).  The
+ * pages quantise only Q and K; the 8-bit P V product is a variant whose
+ * reading is stated here.  A block is 64 consecutive keys of one (b, h) times
+ * all D columns.  With a = max |v| over the block, the scale is 2^e, e the
+ * smallest integer with a <= 448 * 2^e, clamped to [-126, 126] (e = 0 for an
+ * all-zero block); code = E4M3(v * 2^-e), round-half-even (the scaling is
+ * exact, no value saturates).  The power-of-two scale is what the gfx950
+ * scaled matrix instruction applies exactly.
+ *
+ * v        [B, H, S, D] 16-bit (v_dtype LAMP_F16 or LAMP_BF16) at element
+ *          strides (sb, sh, ss, 1); 16-byte aligned, strides multiples of 8.
+ * seqlens  [B] int32 (device, 4-byte aligned) or NULL: keys at or past
+ *          seqlens[b] (clamped to [0, S]) are padding, count as zeros and
+ *          get code 0.
+ * codes    tile-packed, [B, H, ceil(S / 64), D, 64] bytes, 16-byte aligned:
+ *          tile t, row d, position j = 32 c + p (c in {0, 1}, p < 32) holds
+ *          the code of key 64 t + 32 (p / 16) + 8 ((p % 16) / 4) + p % 4 + 4 c,
+ *          column d (keys past S: 0).  This is the order in which the
+ *          kernel's score registers hold a row's 64 keys.
+ * scales   [B, H, ceil(S / 64)] fp32, each exactly 2^e.
+ * D        64, 128 or 256.
+ */
+lamp_status lamp_quantize_v_tiles(const void* v, int32_t v_dtype, int64_t B, int64_t H,
+                                  int64_t S, int64_t D, int64_t sb, int64_t sh, int64_t ss,
+                                  const int32_t* seqlens, void* codes, float* scales,
+                                  void* stream);
 
 /*
  * lamp_build_mask -- the random packed precision mask.
@@ -182,7 +213,13 @@ lamp_status lamp_build_mask_template(int64_t B, int64_t Hq, int64_t S_q, int64_t
  *   - p = exp(s - m_new) on 16-bit elements; on 8-bit elements
  *     p = e4m3(exp(e4m3(max(s - m_new, -448)))) when exp8, else exp(s - m_new);
  *   - l = alpha*l + sum p;  acc = alpha*acc + p V;  O = acc / l at the end.
- * V is never quantised; P V runs at 16 bits on both paths.
+ * P V runs at 16 bits on both paths, unless pv8 = 1 (a variant the pages do
+ * not specify; needs exp8 = 1 and MODE_MASK): then on 8-bit tiles the e4m3
+ * weights p multiply V codes from lamp_quantize_v_tiles,
+ *     acc = alpha*acc + sum_j p_ij * code_j * 2^e(tile),
+ * in an fp8 x fp8 matrix product with fp32 accumulation; 16-bit tiles keep
+ * the 16-bit V.  v8 [B, Hkv, ceil(S_k/64), D, 64] and v_scale
+ * [B, Hkv, ceil(S_k/64)] are then required.
  *
  * Supported: D in {64, 128, 256}; tile_m in {64, 128}; tile_n == 64;
  * in_dtype LAMP_F16 or LAMP_BF16 (q, k, v, out share it); code_dtype LAMP_I8
@@ -238,6 +275,9 @@ typedef struct {
   int32_t* dbg_qk_acc;      /* optional, int8 path                           */
   const int32_t* seqlens_q; /* optional [B], variable-length batch           */
   const int32_t* seqlens_k; /* optional [B]                                  */
+  int32_t pv8;              /* 1: 8-bit P V on 8-bit tiles (exp8, MODE_MASK) */
+  const void* v8;           /* pv8: tile-packed V codes                      */
+  const float* v_scale;     /* pv8: V block scales (powers of two)           */
 } lamp_attn_params;
 
 lamp_status lamp_attn_fwd(const lamp_attn_params* p, void* stream);

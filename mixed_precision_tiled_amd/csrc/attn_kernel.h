@@ -58,7 +58,11 @@ struct AttnShape {
   static constexpr int JK16 = K16_BYTES / 1024 / NW;
   static constexpr int JK8 = K8_BYTES / 1024 / NW;
   static constexpr int JV = V_BYTES / 1024 / NW;
+  // 8-bit P V: tile-packed e4m3 V, D rows of 64 keys
+  static constexpr int V8_BYTES = D * 64;
+  static constexpr int JV8 = V8_BYTES / 1024 / NW;
   static_assert(K8_BYTES % (1024 * NW) == 0, "K8 tile must split evenly over the waves");
+  static_assert(V8_BYTES % (1024 * NW) == 0, "V8 tile must split evenly over the waves");
 };
 
 // LDS layouts.  Every region is row-major (one key per row) in 16-byte chunks;
@@ -68,7 +72,9 @@ struct AttnShape {
 //    positions, so 16 consecutive rows read the same logical chunk without
 //    bank conflicts;
 //  * V rows are read by ds_read_b64_tr_b16 with four consecutive rows per
-//    16-lane group: swz(r) moves rows r..r+3 to distinct bank quads.
+//    16-lane group: swz(r) moves rows r..r+3 to distinct bank quads;
+//  * V8 rows (64 bytes, one head-dim column of the tile-packed 8-bit V) are
+//    read by ds_read_b128 with one row per lane, like K8.
 template <int D>
 struct AttnSwizzle {
   static constexpr int RP16 = 256 / (2 * D) > 1 ? 256 / (2 * D) : 1;   // rows per 256 B
@@ -78,6 +84,11 @@ struct AttnSwizzle {
   __device__ static constexpr int k16(int r) { return (r / RP16) & M16; }
   __device__ static constexpr int k8(int r) { return (r / RP8) & M8; }
   __device__ static constexpr int v(int r) { return D == 64 ? 4 * ((r >> 1) & 1) : 4 * (r & 3); }
+  __device__ static constexpr int v8(int r) { return (r >> 2) & 3; }
+  // row periods of the swizzles
+  static constexpr int P16 = RP16 * (M16 + 1);
+  static constexpr int P8 = RP8 * (M8 + 1);
+  static constexpr int PV = 4;
 };
 
 // Waves per SIMD the register budget is sized for: two for D <= 128 so that
@@ -87,11 +98,12 @@ struct AttnOccupancy {
   static constexpr int kWavesPerEU = D <= 128 ? 2 : 1;
 };
 
-template <int D, int NW, bool BF16, bool E4M3, bool ADAPTIVE, bool EXP8, bool DBG>
+template <int D, int NW, bool BF16, bool E4M3, bool ADAPTIVE, bool EXP8, bool PV8, bool DBG>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(AttnOccupancy<D>::kWavesPerEU, AttnOccupancy<D>::kWavesPerEU)))
 void attn_fwd_kernel(const AttnArgs a) {
   using SH = AttnShape<D, NW>;
+  static_assert(!PV8 || (EXP8 && !ADAPTIVE), "8-bit P V needs 8-bit weights and mask routing");
   // base-2 logits with a lazily moved reference maximum (exact in exact
   // arithmetic); used whenever no 8-bit rounding or flag decision depends on
   // the running maximum
@@ -185,22 +197,41 @@ void attn_fwd_kernel(const AttnArgs a) {
   // position ^ swz(row).  Source offsets inside a tile are per-lane
   // constants; a tile adds key0 * row_stride to the (uniform) base. ----
   using SW = AttnSwizzle<D>;
-  uint32_t off_k16[SH::JK16], off_k8[SH::JK8], off_v[SH::JV];
+  // Copy j + 1 of a region starts RS rows after copy j.  When RS is a
+  // multiple of the region's swizzle period, every copy's per-lane offset is
+  // the first copy's plus j * RS rows: one register serves all copies.
+  constexpr int RS16 = (64 / SH::CH16) * NW, RS8 = (64 / SH::CH8) * NW;
+  constexpr bool K16_1 = RS16 % SW::P16 == 0, K8_1 = RS8 % SW::P8 == 0, V_1 = RS16 % SW::PV == 0;
+  uint32_t off_k16[K16_1 ? 1 : SH::JK16], off_k8[K8_1 ? 1 : SH::JK8], off_v[V_1 ? 1 : SH::JV];
 #pragma unroll
-  for (int j = 0; j < SH::JK16; ++j) {
+  for (int j = 0; j < (K16_1 ? 1 : SH::JK16); ++j) {
     const int p = 64 * (w + NW * j) + lane, r = p / SH::CH16;
     off_k16[j] = (uint32_t)r * kss + (uint32_t)(((p % SH::CH16) ^ SW::k16(r)) << 4);
   }
 #pragma unroll
-  for (int j = 0; j < SH::JK8; ++j) {
+  for (int j = 0; j < (K8_1 ? 1 : SH::JK8); ++j) {
     const int p = 64 * (w + NW * j) + lane, r = p / SH::CH8;
     off_k8[j] = (uint32_t)(r * D + (((p % SH::CH8) ^ SW::k8(r)) << 4));
   }
 #pragma unroll
-  for (int j = 0; j < SH::JV; ++j) {
+  for (int j = 0; j < (V_1 ? 1 : SH::JV); ++j) {
     const int p = 64 * (w + NW * j) + lane, r = p / SH::CH16;
     off_v[j] = (uint32_t)r * vss + (uint32_t)(((p % SH::CH16) ^ SW::v(r)) << 4);
   }
+  // offset of copy j (the empty asm keeps the sums from being hoisted out
+  // of the loop into registers of their own)
+  auto copy_off = [](const uint32_t* off, bool one, int j, uint32_t row_step_bytes) -> uint32_t {
+    if (!one) return off[j];
+    uint32_t o = off[0];
+    asm volatile("" : "+v"(o));
+    return o + (uint32_t)j * row_step_bytes;
+  };
+  // tile-packed V8: copy n fills rows 16n .. 16n+15 (4 chunks of 16 bytes
+  // each); lane l fills row 16n + l/4, position l%4, and swz of that row is
+  // (l/16)%4 for every n, so one per-lane offset serves all copies
+  const uint32_t off_v8 = (uint32_t)((lane >> 2) * 64 + (((lane & 3) ^ ((lane >> 4) & 3)) << 4));
+  const uint8_t* v8base = PV8 ? a.v8 + ((int64_t)b * a.Hkv + kvh) * a.n_kt * SH::V8_BYTES : nullptr;
+  const float* sVp = PV8 ? a.v_scale + ((int64_t)b * a.Hkv + kvh) * a.n_kt : nullptr;
   // each tile's copies go through buffer resources that start at the tile's
   // first row and end with the head's last row: per-lane offsets past S_k
   // (ragged last tile) fall outside the resource and read zeros, which are
@@ -213,18 +244,32 @@ void attn_fwd_kernel(const AttnArgs a) {
     if (is8) {
       const auto rs = make_rsrc(k8base + key0 * D, k8_bytes - key0 * D);
 #pragma unroll
-      for (int j = 0; j < SH::JK8; ++j) dma16_buf(rs, off_k8[j], 0u, kdst + 1024 * (w + NW * j));
+      for (int j = 0; j < SH::JK8; ++j)
+        dma16_buf(rs, copy_off(off_k8, K8_1, j, (uint32_t)(RS8 * D)), 0u, kdst + 1024 * (w + NW * j));
     } else {
       const auto rs = make_rsrc(kbase + key0 * kss, k16_bytes - key0 * kss);
 #pragma unroll
-      for (int j = 0; j < SH::JK16; ++j) dma16_buf(rs, off_k16[j], 0u, kdst + 1024 * (w + NW * j));
+      for (int j = 0; j < SH::JK16; ++j)
+        dma16_buf(rs, copy_off(off_k16, K16_1, j, (uint32_t)RS16 * kss), 0u, kdst + 1024 * (w + NW * j));
     }
   };
-  auto issue_v = [&](int kt, char* vdst) {
+  auto issue_v = [&](int kt, bool is8, char* vdst) {
+    if constexpr (PV8) {
+      if (is8) {
+        // whole tiles, always in bounds (the quantiser zero-fills keys past
+        // the sequence)
+        const uint8_t* src = v8base + (int64_t)kt * SH::V8_BYTES;
+#pragma unroll
+        for (int j = 0; j < SH::JV8; ++j)
+          dma16(src + 1024 * (w + NW * j) + off_v8, vdst + 1024 * (w + NW * j));
+        return;
+      }
+    }
     const uint32_t key0 = (uint32_t)(kt * SH::TN);
     const auto rv = make_rsrc(vbase + key0 * vss, v_bytes - key0 * vss);
 #pragma unroll
-    for (int j = 0; j < SH::JV; ++j) dma16_buf(rv, off_v[j], 0u, vdst + 1024 * (w + NW * j));
+    for (int j = 0; j < SH::JV; ++j)
+      dma16_buf(rv, copy_off(off_v, V_1, j, (uint32_t)RS16 * vss), 0u, vdst + 1024 * (w + NW * j));
   };
 
   // ---- per-lane LDS read offsets ----
@@ -446,6 +491,23 @@ void attn_fwd_kernel(const AttnArgs a) {
     }
   };
 
+  // (2') 8-bit P V: O^T += V8^T P8^T * 2^e for a tile whose e4m3 weights are
+  //      pk[0..7] (lane: query row lr, keys in score-register order, which
+  //      is the tile-packed V8 key order); one K = 64 fp8 product per 32
+  //      head-dim rows, the tile's power-of-two V scale as operand A's E8M0
+  //      block scale
+  auto pv8_part = [&](const char* vb, const uint32_t* pk, int svc) {
+    const u32x4 p0 = {pk[0], pk[1], pk[2], pk[3]}, p1 = {pk[4], pk[5], pk[6], pk[7]};
+    const int sw = SW::v8(lr);
+#pragma unroll
+    for (int db = 0; db < SH::ND; ++db) {
+      const char* row = vb + (db * 32 + lr) * 64;
+      const u32x4 a0 = ld_lds16(row + (((2 * hf) ^ sw) << 4));
+      const u32x4 a1 = ld_lds16(row + (((2 * hf + 1) ^ sw) << 4));
+      O[db] = mfma_e4m3_sa(a0, a1, p0, p1, O[db], svc);
+    }
+  };
+
   // Instruction order for the block holding P V of tile kt-1 and the
   // softmax of tile kt: a wave issues in order and an MFMA waits for the
   // matrix pipe, so the 16 MFMAs are spread over the softmax arithmetic
@@ -463,9 +525,13 @@ void attn_fwd_kernel(const AttnArgs a) {
   };
 
   // (3) shared online-softmax update with the logits of tile kt; writes the
-  //     16-bit weights to pk.  Any rescale of O applies to everything
-  //     accumulated so far, P V of the previous tile included.
-  auto softmax_part = [&](float* x, const Logits& lg, uint32_t* pk) {
+  //     weights to pk (16-bit pairs, or with the 8-bit P V on an 8-bit tile
+  //     the e4m3 codes in pk[0..7]).  Any rescale of O applies to everything
+  //     accumulated so far, P V of the previous tile included.  pvc: whether
+  //     the block also holds the (16-bit) P V of the previous tile, whose
+  //     products are then spread over the softmax arithmetic.
+  auto softmax_part = [&](float* x, const Logits& lg, uint32_t* pk, auto pvc) {
+    constexpr bool WITH_PV = decltype(pvc)::value;
     const float cm = lg.scaled ? 1.f : lg.c;
     const float xoff = lg.xoff;
     float mx = x[0];
@@ -473,8 +539,19 @@ void attn_fwd_kernel(const AttnArgs a) {
     for (int e = 1; e < 32; ++e) mx = fmaxf(mx, x[e]);
     mx = (mx - xoff) * cm;
     mx = halves_max(mx);
-    // the 16-bit weights go to pk (the fp32 weights overwrite x in place)
-    auto weights = [&](float mref) {
+    // the normaliser sums exactly the rounded weights that feed P V
+    auto psum = [&](const uint32_t* w16) {
+      float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        ps0 = sum16x2<BF16>(w16[i], ps0);
+        ps1 = sum16x2<BF16>(w16[i + 1], ps1);
+      }
+      return ps0 + ps1;
+    };
+    // the weights go to pk (the fp32 weights overwrite x in place); returns
+    // their sum
+    auto weights = [&](float mref) -> float {
       if constexpr (LAZY) {
         // exp2((x - xoff) * cm - m) with the offset folded into the constant
         const float msub = ((mref == kNegInf) ? 0.f : mref) + xoff * cm;
@@ -484,8 +561,10 @@ void attn_fwd_kernel(const AttnArgs a) {
         const float msub = (mref == kNegInf) ? 0.f : mref;
         if (EXP8 && !lg.is16) {
           // x = s - m rounded to e4m3, exp, rounded to e4m3 again; four
-          // values per code word, the final codes converted straight to the
-          // 16-bit P operand
+          // values per code word.  The final codes are the 8-bit P operand,
+          // or are converted straight to the 16-bit one.
+          // (the sum in the order of psum: even words, odd words)
+          float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
           for (int e = 0; e < 32; e += 4) {
             float xs[4];
@@ -495,10 +574,23 @@ void attn_fwd_kernel(const AttnArgs a) {
             const f32x2 xlo = e4m3x2_to_f32<false>(xc), xhi = e4m3x2_to_f32<true>(xc);
             const uint32_t pc = f32x4_to_e4m3(exp2_fast(xlo.x * kLog2e), exp2_fast(xlo.y * kLog2e),
                                               exp2_fast(xhi.x * kLog2e), exp2_fast(xhi.y * kLog2e));
-            pk[e >> 1] = e4m3x2_to_16<BF16, false>(pc);
-            pk[(e >> 1) + 1] = e4m3x2_to_16<BF16, true>(pc);
+            const uint32_t lo16 = e4m3x2_to_16<BF16, false>(pc), hi16 = e4m3x2_to_16<BF16, true>(pc);
+            if constexpr (PV8) {
+              pk[e >> 2] = pc;
+            } else {
+              pk[e >> 1] = lo16;
+              pk[(e >> 1) + 1] = hi16;
+            }
+            ps0 = sum16x2<BF16>(lo16, ps0);
+            ps1 = sum16x2<BF16>(hi16, ps1);
           }
-          return;
+          if constexpr (PV8) {
+            // pk[8..15] are not read by the 8-bit product: let the old
+            // 16-bit weights die instead of carrying them through
+#pragma unroll
+            for (int i = 8; i < 16; ++i) pk[i] = __builtin_nondeterministic_value(pk[i]);
+          }
+          return ps0 + ps1;
         } else {
           const float c2 = cm * kLog2e, m2 = msub * kLog2e;
 #pragma unroll
@@ -507,16 +599,7 @@ void attn_fwd_kernel(const AttnArgs a) {
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) pk[i] = pack16x2<BF16>(x[2 * i], x[2 * i + 1]);
-    };
-    auto psum = [&]() {
-      // the normaliser sums exactly the rounded weights that feed P V
-      float ps0 = 0.f, ps1 = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        ps0 = sum16x2<BF16>(pk[i], ps0);
-        ps1 = sum16x2<BF16>(pk[i + 1], ps1);
-      }
-      return ps0 + ps1;
+      return psum(pk);
     };
     // New reference maximum, chosen before the weights (a select, no
     // branch), so that max, weights, packing and the row sum stay in one
@@ -533,14 +616,15 @@ void attn_fwd_kernel(const AttnArgs a) {
       m_new = fmaxf(m_run, mx);
       move = wave_any(m_new != m_run);
     }
-    weights(m_new);
-    float l_add = psum();
+    float l_add = weights(m_new);
     // the weights must precede the branch (otherwise it is hoisted above
     // them, which splits them off the P V products)
     asm volatile("" : "+v"(l_add));
-    interleave_pv_softmax();
+    if constexpr (WITH_PV) interleave_pv_softmax();
     if (move) {
       __builtin_amdgcn_sched_barrier(0);
+      // an 8-bit P V product may have written O shortly before
+      if constexpr (PV8) xdl16_settle();
       float alpha;
       if constexpr (LAZY) alpha = (m_new == kNegInf) ? 1.f : exp2_fast(m_run - m_new);
       else alpha = (m_run == kNegInf) ? 0.f : exp2_fast((m_run - m_new) * kLog2e);
@@ -563,6 +647,25 @@ void attn_fwd_kernel(const AttnArgs a) {
   for (int i = 0; i < 16; ++i) pk[i] = 0u;
   bool is8_cur = tile_is8(0);
   float sk_cur = ld_uniform(sKp);
+  // route and V scale (E8M0 code) of the tile whose P V is pending
+  bool is8_prev = false;
+  int svc_cur = 127, svc_prev = 127;
+  using True_ = std::integral_constant<bool, true>;
+  using False_ = std::integral_constant<bool, false>;
+  // P V with no softmax to overlap (ragged waves, the last tile)
+  auto pv_tile = [&](const char* vb, bool is8p, int svc) {
+    if constexpr (PV8) {
+      // one-sided blocks, as in the main step
+      int p8 = is8p ? 1 : 0;
+      xdl16_settle();
+      if (p8) pv8_part(vb, pk, svc);
+      xdl16_settle();
+      asm volatile("" : "+s"(p8));
+      if (!p8) pv_part(vb, pk);
+    } else {
+      pv_part(vb, pk);
+    }
+  };
   issue_k(0, is8_cur, sk0);
   wait_vmem();
   __syncthreads();
@@ -576,14 +679,32 @@ void attn_fwd_kernel(const AttnArgs a) {
       sk_next = ld_uniform(sKp + kt + 1);
       issue_k(kt + 1, is8_next, knxt);
     }
-    issue_v(kt, vcur);
+    if constexpr (PV8) {
+      if (is8_cur) svc_cur = (int)((__builtin_bit_cast(uint32_t, ld_uniform(sVp + kt)) >> 23) & 0xFFu);
+    }
+    issue_v(kt, is8_cur, vcur);
     if (kt < kt_end_w) {
       float x[32];
       const Logits lg = qk_part(kt, kcur, is8_cur, sk_cur, x);
-      if constexpr (!FIRST) pv_part(vprev, pk);
-      softmax_part(x, lg, pk);
+      if constexpr (FIRST) {
+        softmax_part(x, lg, pk, False_{});
+      } else if constexpr (PV8) {
+        // P V of the previous tile (8- or 16-bit), then the softmax.  Two
+        // one-sided blocks instead of an if/else: with both arms updating O
+        // the register allocator gives O different registers in each arm
+        // and copies all of it at the join (and then spills); the opaque
+        // flag keeps the blocks from being merged back into an if/else.
+        int p8 = is8_prev ? 1 : 0;
+        if (p8) pv8_part(vprev, pk, svc_prev);
+        asm volatile("" : "+s"(p8));
+        if (!p8) pv_part(vprev, pk);
+        softmax_part(x, lg, pk, False_{});
+      } else {
+        pv_part(vprev, pk);
+        softmax_part(x, lg, pk, True_{});
+      }
     } else if (!FIRST && kt - 1 < kt_end_w) {
-      pv_part(vprev, pk);
+      pv_tile(vprev, is8_prev, svc_prev);
     }
     if constexpr (ADAPTIVE) {
       if (((kt & 63) == 63) || kt == kt_end - 1) {
@@ -593,11 +714,11 @@ void attn_fwd_kernel(const AttnArgs a) {
     }
     wait_vmem();
     __syncthreads();
+    is8_prev = is8_cur;
+    svc_prev = svc_cur;
     is8_cur = is8_next;
     sk_cur = sk_next;
   };
-  using True_ = std::integral_constant<bool, true>;
-  using False_ = std::integral_constant<bool, false>;
   if (kt_end > 0) step(True_{}, 0, sk0, sk1, sv1, sv0);
   for (int kt = 1; kt < kt_end; kt += 2) {
     step(False_{}, kt, sk1, sk0, sv0, sv1);
@@ -605,8 +726,8 @@ void attn_fwd_kernel(const AttnArgs a) {
   }
   // P V of the last tile (its V was copied in the last step)
   if (kt_end_w == kt_end && kt_end > 0) {
-    if ((kt_end - 1) & 1) pv_part(sv1, pk);
-    else pv_part(sv0, pk);
+    if ((kt_end - 1) & 1) pv_tile(sv1, is8_prev, svc_prev);
+    else pv_tile(sv0, is8_prev, svc_prev);
   }
   if constexpr (ADAPTIVE) {
     if (frow != nullptr && lane == 0) {

@@ -111,6 +111,40 @@ lamp_status lamp_quantize_blocks_varlen(const void* x, int32_t x_dtype, int64_t 
   return hip_status(lamp::launch_quantize(a, static_cast<hipStream_t>(stream)), "quantize launch");
 }
 
+lamp_status lamp_quantize_v_tiles(const void* v, int32_t v_dtype, int64_t B, int64_t H, int64_t S,
+                                  int64_t D, int64_t sb, int64_t sh, int64_t ss,
+                                  const int32_t* seqlens, void* codes, float* scales,
+                                  void* stream) {
+  if (B < 0 || H < 0 || S < 0 || D < 0) return fail(LAMP_ERR_SHAPE, "negative size");
+  if (sb < 0 || sh < 0 || ss < 0) return fail(LAMP_ERR_SHAPE, "negative stride");
+  if (!is16(v_dtype)) return fail(LAMP_ERR_UNSUPPORTED, "v_dtype must be LAMP_F16 or LAMP_BF16");
+  if (!supported_d(D)) return fail(LAMP_ERR_UNSUPPORTED, "D=%lld not in {64,128,256}", (long long)D);
+  if (S > kMaxSeq) return fail(LAMP_ERR_UNSUPPORTED, "S=%lld above %lld", (long long)S, (long long)kMaxSeq);
+  if (B == 0 || H == 0 || S == 0) return ok();
+  if (!v || !codes || !scales) return fail(LAMP_ERR_NULL, "v, codes and scales are required");
+  if (ss < D) return fail(LAMP_ERR_SHAPE, "row stride %lld < D", (long long)ss);
+  if (!aligned16(v) || !aligned16(codes) || (ss % 8) || (sh % 8) || (sb % 8))
+    return fail(LAMP_ERR_ALIGN, "v, codes need 16-byte alignment and strides a multiple of 8");
+  if (reinterpret_cast<uintptr_t>(seqlens) & 3u) return fail(LAMP_ERR_ALIGN, "seqlens needs 4-byte alignment");
+  const int64_t n_kt = cdiv(S, 64);
+  if (B * H * n_kt > kMaxGrid) return fail(LAMP_ERR_UNSUPPORTED, "too many tiles");
+  lamp::VQuantArgs a{};
+  a.v = v;
+  a.codes = static_cast<uint8_t*>(codes);
+  a.scales = scales;
+  a.sb = sb;
+  a.sh = sh;
+  a.ss = ss;
+  a.B = (int32_t)B;
+  a.H = (int32_t)H;
+  a.S = (int32_t)S;
+  a.D = (int32_t)D;
+  a.n_kt = (int32_t)n_kt;
+  a.seqlens = seqlens;
+  a.bf16 = v_dtype == LAMP_BF16;
+  return hip_status(lamp::launch_quantize_v(a, static_cast<hipStream_t>(stream)), "V quantize launch");
+}
+
 lamp_status lamp_build_mask(int64_t B, int64_t Hq, int64_t S_q, int64_t S_k, int32_t tile_m,
                             int32_t tile_n, int32_t tiles_per_bit, double frac_16bit,
                             uint64_t seed, uint64_t* mask, int32_t words_per_row,
@@ -204,6 +238,9 @@ lamp_status lamp_attn_fwd(const lamp_attn_params* p, void* stream) {
   if (p->causal != 0 && p->causal != 1) return fail(LAMP_ERR_SHAPE, "causal must be 0 or 1");
   if (p->causal && p->S_q > p->S_k) return fail(LAMP_ERR_UNSUPPORTED, "causal needs S_q <= S_k");
   if (p->exp8 != 0 && p->exp8 != 1) return fail(LAMP_ERR_SHAPE, "exp8 must be 0 or 1");
+  if (p->pv8 != 0 && p->pv8 != 1) return fail(LAMP_ERR_SHAPE, "pv8 must be 0 or 1");
+  if (p->pv8 && (!p->exp8 || p->mode != LAMP_MODE_MASK))
+    return fail(LAMP_ERR_UNSUPPORTED, "pv8 needs exp8 = 1 and LAMP_MODE_MASK");
   if (p->mode == LAMP_MODE_ADAPTIVE) {
     if (p->sub_rows != 32) return fail(LAMP_ERR_UNSUPPORTED, "sub_rows must be 32");
     if (std::isnan(p->tau)) return fail(LAMP_ERR_SHAPE, "tau is NaN");
@@ -237,6 +274,11 @@ lamp_status lamp_attn_fwd(const lamp_attn_params* p, void* stream) {
     return fail(LAMP_ERR_ALIGN, "seqlens need 4-byte alignment");
   if (p->flags_out && (reinterpret_cast<uintptr_t>(p->flags_out) & 7u))
     return fail(LAMP_ERR_ALIGN, "flags_out alignment");
+  if (p->pv8) {
+    if (!p->v8 || !p->v_scale) return fail(LAMP_ERR_NULL, "pv8 needs v8 and v_scale");
+    if (!aligned16(p->v8)) return fail(LAMP_ERR_ALIGN, "v8 needs 16-byte alignment");
+    if (reinterpret_cast<uintptr_t>(p->v_scale) & 3u) return fail(LAMP_ERR_ALIGN, "v_scale alignment");
+  }
   if (p->B * p->Hq * n_qt > kMaxGrid) return fail(LAMP_ERR_UNSUPPORTED, "grid too large");
   // K and V rows of one head are addressed with 32-bit byte offsets
   if (2 * p->S_k * p->k_str[2] >= (int64_t(1) << 31) || 2 * p->S_k * p->v_str[2] >= (int64_t(1) << 31))
@@ -257,6 +299,8 @@ lamp_status lamp_attn_fwd(const lamp_attn_params* p, void* stream) {
   a.dbg = p->dbg_qk_acc;
   a.seqlens_q = p->seqlens_q;
   a.seqlens_k = p->seqlens_k;
+  a.v8 = p->pv8 ? static_cast<const uint8_t*>(p->v8) : nullptr;
+  a.v_scale = p->pv8 ? p->v_scale : nullptr;
   a.q_sb = p->q_str[0];
   a.q_sh = p->q_str[1];
   a.q_ss = p->q_str[2];
@@ -292,6 +336,7 @@ lamp_status lamp_attn_fwd(const lamp_attn_params* p, void* stream) {
   c.e4m3 = p->code_dtype == LAMP_E4M3;
   c.adaptive = p->mode == LAMP_MODE_ADAPTIVE;
   c.exp8 = p->exp8 != 0;
+  c.pv8 = p->pv8 != 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   switch (c.d) {

@@ -64,6 +64,15 @@ __device__ __forceinline__ f32x16 mfma_e4m3(u32x4 a0, u32x4 a1, u32x4 b0, u32x4 
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+// The same product with a power-of-two scale 2^(sa - 127) on operand A (sa
+// is the E8M0 code, i.e. the biased exponent field of an fp32 power of two).
+__device__ __forceinline__ f32x16 mfma_e4m3_sa(u32x4 a0, u32x4 a1, u32x4 b0, u32x4 b1, f32x16 c,
+                                               int sa) {
+  i32x8 a = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+  i32x8 b = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, 127);
+}
+
 // ---------------------------------------------------------------------------
 // conversions
 // ---------------------------------------------------------------------------

@@ -19,6 +19,16 @@ struct QuantArgs {
   bool bf16, e4m3;
 };
 
+struct VQuantArgs {
+  const void* v;
+  uint8_t* codes;              // [B, H, n_kt, D, 64] tile-packed
+  float* scales;               // [B, H, n_kt]
+  int64_t sb, sh, ss;          // element strides of v
+  int32_t B, H, S, D, n_kt;
+  const int32_t* seqlens;      // [B] or nullptr (all S)
+  bool bf16;
+};
+
 struct MaskArgs {
   uint64_t* mask;
   int64_t total_words;         // B * Hq * n_qt * words_per_row
@@ -55,6 +65,8 @@ struct AttnArgs {
   int32_t* dbg;
   const int32_t* seqlens_q;    // [B] or nullptr (all S_q)
   const int32_t* seqlens_k;    // [B] or nullptr (all S_k)
+  const uint8_t* v8;           // pv8: [B, Hkv, n_kt, D, 64] tile-packed e4m3 V
+  const float* v_scale;        // pv8: [B, Hkv, n_kt] powers of two
   int64_t q_sb, q_sh, q_ss;
   int64_t k_sb, k_sh, k_ss;
   int64_t v_sb, v_sh, v_ss;
@@ -99,9 +111,11 @@ struct AttnConfig {
   bool e4m3;
   bool adaptive;
   bool exp8;
+  bool pv8;
 };
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
+hipError_t launch_quantize_v(const VQuantArgs& a, hipStream_t s);
 hipError_t launch_build_mask(const MaskArgs& a, hipStream_t s);
 hipError_t launch_build_mask_template(const TemplateMaskArgs& a, hipStream_t s);
 hipError_t launch_attn_d64(const AttnArgs& a, const AttnConfig& c, hipStream_t s);

@@ -1,4 +1,4 @@
-// Per-block Q/K quantiser and random packed-mask builder (gfx950).
+// Per-block Q/K quantiser, V tile quantiser and mask builders (gfx950).
 //
 // Quantiser: TileMix page, section 2 "The Dual-Path Engine" (Q and K
 // quantised with per-block scale factors); LampAttention abstract (8-bit
@@ -114,6 +114,93 @@ hipError_t launch_quant_t(const QuantArgs& a, int cpt, hipStream_t s) {
   return hipGetLastError();
 }
 
+// V for the 8-bit P V product: one workgroup per (b, h, 64-key tile), e4m3
+// codes with one power-of-two scale 2^e per tile (e the smallest integer with
+// absmax <= 448 * 2^e, clamped to [-126, 126]; 0 for an all-zero tile).  The
+// output is tile-packed: row d of the tile holds the 64 keys of column d in
+// the order of the attention kernel's score registers (position 32 c + p,
+// key 32 (p / 16) + 8 ((p % 16) / 4) + p % 4 + 4 c).  Thread t owns the
+// half-rows hr = t + 256 i (column hr % D, half hr / D): consecutive threads
+// read consecutive columns of one key row, then write 32 contiguous bytes.
+template <bool BF16, int D>
+__global__ __launch_bounds__(kQuantThreads) void quantize_v_kernel(VQuantArgs a) {
+  constexpr int HRT = (2 * D + kQuantThreads - 1) / kQuantThreads;
+  const int kt = blockIdx.x % a.n_kt;
+  const int bh = blockIdx.x / a.n_kt;
+  const int h = bh % a.H;
+  const int b = bh / a.H;
+  // keys at or past the sequence length are padding: not read, zero
+  const int len = a.seqlens != nullptr ? min(max(ld_uniform(a.seqlens + b), 0), a.S) : a.S;
+  const char* base = reinterpret_cast<const char*>(a.v) + 2 * (b * a.sb + h * a.sh);
+  const int tid = threadIdx.x;
+
+  float val[HRT][32];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < HRT; ++i) {
+    const int hr = tid + i * kQuantThreads;
+    const int d = hr % D, c = hr / D;
+#pragma unroll
+    for (int p = 0; p < 32; ++p) {
+      const int key = kt * 64 + 32 * (p >> 4) + 8 * ((p & 15) >> 2) + (p & 3) + 4 * c;
+      float x = 0.f;
+      if (hr < 2 * D && key < len)
+        x = from16<BF16>(*reinterpret_cast<const uint16_t*>(base + 2 * ((int64_t)key * a.ss + d)));
+      val[i][p] = x;
+      amax = fmaxf(amax, fabsf(x));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  __shared__ float red[kQuantThreads / 64];
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = red[0];
+#pragma unroll
+  for (int w = 1; w < kQuantThreads / 64; ++w) amax = fmaxf(amax, red[w]);
+
+  // amax = f * 2^k, f in [0.5, 1); 448 = 0.875 * 2^9
+  int e = 0;
+  if (amax > 0.f) {
+    int k;
+    const float f = frexpf(amax, &k);
+    e = min(max(k - 9 + (f > 0.875f ? 1 : 0), -126), 126);
+  }
+  const float inv = __builtin_bit_cast(float, (uint32_t)(127 - e) << 23);   // 2^-e, exact
+  if (tid == 0)
+    a.scales[((int64_t)b * a.H + h) * a.n_kt + kt] = __builtin_bit_cast(float, (uint32_t)(127 + e) << 23);
+
+  uint8_t* out = a.codes + (((int64_t)b * a.H + h) * a.n_kt + kt) * (int64_t)(D * 64);
+#pragma unroll
+  for (int i = 0; i < HRT; ++i) {
+    const int hr = tid + i * kQuantThreads;
+    if (hr >= 2 * D) continue;
+    const int d = hr % D, c = hr / D;
+    uint32_t wd[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      // an all-zero tile encodes as +0 whatever the sign of its zeros
+      wd[q] = amax > 0.f ? f32x4_to_e4m3(val[i][4 * q] * inv, val[i][4 * q + 1] * inv,
+                                         val[i][4 * q + 2] * inv, val[i][4 * q + 3] * inv)
+                         : 0u;
+    }
+    char* dst = reinterpret_cast<char*>(out + d * 64 + 32 * c);
+    *reinterpret_cast<u32x4*>(dst) = u32x4{wd[0], wd[1], wd[2], wd[3]};
+    *reinterpret_cast<u32x4*>(dst + 16) = u32x4{wd[4], wd[5], wd[6], wd[7]};
+  }
+}
+
+template <bool BF16>
+hipError_t launch_quant_v_t(const VQuantArgs& a, hipStream_t s) {
+  dim3 grid((unsigned)((int64_t)a.B * a.H * a.n_kt)), block(kQuantThreads);
+  switch (a.D) {
+    case 64: hipLaunchKernelGGL((quantize_v_kernel<BF16, 64>), grid, block, 0, s, a); break;
+    case 128: hipLaunchKernelGGL((quantize_v_kernel<BF16, 128>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((quantize_v_kernel<BF16, 256>), grid, block, 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
 __device__ __forceinline__ uint64_t splitmix64(uint64_t seed, uint64_t n) {
   uint64_t z = seed + (n + 1ull) * 0x9E3779B97F4A7C15ull;
   z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
@@ -172,6 +259,10 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
     return a.e4m3 ? launch_quant_t<true, true>(a, cpt, s) : launch_quant_t<true, false>(a, cpt, s);
   }
   return a.e4m3 ? launch_quant_t<false, true>(a, cpt, s) : launch_quant_t<false, false>(a, cpt, s);
+}
+
+hipError_t launch_quantize_v(const VQuantArgs& a, hipStream_t s) {
+  return a.bf16 ? launch_quant_v_t<true>(a, s) : launch_quant_v_t<false>(a, s);
 }
 
 hipError_t launch_build_mask(const MaskArgs& a, hipStream_t s) {

@@ -52,6 +52,7 @@ class lamp_attn_params(ctypes.Structure):
         ("exp8", _i32), ("tau", ctypes.c_float), ("sub_rows", _i32),
         ("out", _vp), ("lse", _vp), ("flags_out", _vp), ("dbg_qk_acc", _vp),
         ("seqlens_q", _vp), ("seqlens_k", _vp),
+        ("pv8", _i32), ("v8", _vp), ("v_scale", _vp),
     ]
 
 
@@ -61,6 +62,9 @@ _lib.lamp_quantize_blocks.argtypes = [_vp, _i32, _i64, _i64, _i64, _i64, _i64, _
 _lib.lamp_quantize_blocks_varlen.restype = _i32
 _lib.lamp_quantize_blocks_varlen.argtypes = [_vp, _i32, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                              _vp, _i32, _i32, _vp, _vp, _vp]
+_lib.lamp_quantize_v_tiles.restype = _i32
+_lib.lamp_quantize_v_tiles.argtypes = [_vp, _i32, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _vp,
+                                       _vp, _vp, _vp]
 _lib.lamp_build_mask.restype = _i32
 _lib.lamp_build_mask.argtypes = [_i64, _i64, _i64, _i64, _i32, _i32, _i32, ctypes.c_double, _u64,
                                  _vp, _i32, _vp]
@@ -154,6 +158,29 @@ def lamp_quantize_blocks(x, block_rows, code, codes=None, scales=None, seqlens=N
     return codes, scales
 
 
+def lamp_quantize_v_tiles(v, codes=None, scales=None, seqlens=None):
+    """V [B, H, S, D] (fp16/bf16 CUDA tensor) as e4m3 codes for the 8-bit P V
+    product.  Returns (codes uint8 [B, H, ceil(S/64), D, 64] tile-packed,
+    scales float32 [B, H, ceil(S/64)], each a power of two)."""
+    B, H, S, D = v.shape
+    nt = cdiv(S, 64)
+    if codes is None:
+        codes = torch.empty((B, H, nt, D, 64), dtype=torch.uint8, device=v.device)
+    if scales is None:
+        scales = torch.empty((B, H, nt), dtype=torch.float32, device=v.device)
+    if v.dtype not in _DT16:
+        raise TypeError("v must be float16 or bfloat16")
+    if v.stride(3) != 1 or not codes.is_contiguous() or not scales.is_contiguous():
+        raise ValueError("v needs a contiguous head dim; codes and scales must be contiguous")
+    if seqlens is not None and (seqlens.dtype != torch.int32 or tuple(seqlens.shape) != (B,)
+                                or not seqlens.is_contiguous()):
+        raise ValueError("seqlens must be a contiguous int32 tensor [B]")
+    _check(_lib.lamp_quantize_v_tiles(_ptr(v), _DT16[v.dtype], B, H, S, D, v.stride(0), v.stride(1),
+                                      v.stride(2), _ptr(seqlens), _ptr(codes), _ptr(scales),
+                                      _stream(v)))
+    return codes, scales
+
+
 def lamp_build_mask(B, Hq, S_q, S_k, tile_m, tile_n, tiles_per_bit, frac_16bit, seed,
                     words_per_row=None, mask=None, device="cuda"):
     """Random packed mask, int64 tensor [B, Hq, n_qt, W] holding the uint64 words."""
@@ -190,11 +217,13 @@ def lamp_build_mask_template(B, Hq, S_q, S_k, tile_m, tile_n, tiles_per_bit, sin
 def lamp_attn_fwd(q, k, v, q8, k8, q_scale, k_scale, mask, *, code, causal, tile_m,
                   tiles_per_bit, tile_n=64, words_per_row=None, mode=LAMP_MODE_MASK, exp8=False,
                   tau=4.0, sub_rows=32, sm_scale=0.0, out=None, lse=None, flags_out=None,
-                  dbg_qk_acc=None, seqlens_q=None, seqlens_k=None):
+                  dbg_qk_acc=None, seqlens_q=None, seqlens_k=None, v8=None, v_scale=None):
     """Dual-path attention forward.  q [B,Hq,S_q,D], k/v [B,Hkv,S_k,D] 16-bit,
     q8/k8 codes and q_scale/k_scale from lamp_quantize_blocks, mask from
     lamp_build_mask.  Returns out [B,Hq,S_q,D] (q's dtype).  seqlens_q /
-    seqlens_k: optional int32 tensors [B] of a variable-length batch."""
+    seqlens_k: optional int32 tensors [B] of a variable-length batch.
+    v8 / v_scale (from lamp_quantize_v_tiles) select the 8-bit P V product
+    on 8-bit tiles (with exp8 and mask routing)."""
     B, Hq, S_q, D = q.shape
     _, Hkv, S_k, _ = k.shape
     if q.dtype not in _DT16 or k.dtype != q.dtype or v.dtype != q.dtype:
@@ -202,7 +231,10 @@ def lamp_attn_fwd(q, k, v, q8, k8, q_scale, k_scale, mask, *, code, causal, tile
     if out is None:
         out = torch.empty((B, Hq, S_q, D), dtype=q.dtype, device=q.device)
     W = words_per_row or mask.shape[-1]
-    for t in (q8, k8, q_scale, k_scale, mask, lse, flags_out, dbg_qk_acc, seqlens_q, seqlens_k):
+    if (v8 is None) != (v_scale is None):
+        raise ValueError("v8 and v_scale go together")
+    for t in (q8, k8, q_scale, k_scale, mask, lse, flags_out, dbg_qk_acc, seqlens_q, seqlens_k,
+              v8, v_scale):
         if t is not None and not t.is_contiguous():
             raise ValueError("codes, scales, mask and optional outputs must be contiguous")
     for t in (seqlens_q, seqlens_k):
@@ -232,6 +264,9 @@ def lamp_attn_fwd(q, k, v, q8, k8, q_scale, k_scale, mask, *, code, causal, tile
     p.dbg_qk_acc = None if dbg_qk_acc is None else dbg_qk_acc.data_ptr()
     p.seqlens_q = None if seqlens_q is None else seqlens_q.data_ptr()
     p.seqlens_k = None if seqlens_k is None else seqlens_k.data_ptr()
+    p.pv8 = int(v8 is not None)
+    p.v8 = None if v8 is None else v8.data_ptr()
+    p.v_scale = None if v_scale is None else v_scale.data_ptr()
     _check(_lib.lamp_attn_fwd(ctypes.byref(p), _stream(q)))
     return out
 

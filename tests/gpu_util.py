@@ -15,8 +15,9 @@ def u64(t):
     return t.cpu().numpy().view(np.uint64)
 
 
-def gpu_run(cfg, q, k, v, *, lse=True, flags=None, dbg=False, mask_words=None):
-    """Quantise, build the mask (unless given) and run attention on the GPU."""
+def gpu_run(cfg, q, k, v, *, lse=True, flags=None, dbg=False, mask_words=None, pv8=False):
+    """Quantise, build the mask (unless given) and run attention on the GPU
+    (pv8: V tiles quantised too, 8-bit P V on 8-bit tiles)."""
     import mixed_precision_tiled_amd as L
     dev = device()
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
@@ -41,17 +42,23 @@ def gpu_run(cfg, q, k, v, *, lse=True, flags=None, dbg=False, mask_words=None):
     dbg_t = None
     if dbg:
         dbg_t = torch.full((cfg.B, cfg.Hq, S_q, S_k), -(2 ** 31), dtype=torch.int32, device=dev)
+    v8 = vs = None
+    if pv8:
+        v8, vs = L.lamp_quantize_v_tiles(vd)
     out = L.lamp_attn_fwd(qd, kd, vd, q8, k8, sq, sk, mask, code=cfg.code, causal=cfg.causal,
                           tile_m=cfg.tile_m, tiles_per_bit=cfg.tiles_per_bit,
                           mode=L.LAMP_MODE_ADAPTIVE if cfg.adaptive else L.LAMP_MODE_MASK,
                           exp8=cfg.exp8, tau=cfg.tau, sub_rows=cfg.sub_rows,
-                          sm_scale=cfg.sm_scale, lse=lse_t, flags_out=flags_t, dbg_qk_acc=dbg_t)
+                          sm_scale=cfg.sm_scale, lse=lse_t, flags_out=flags_t, dbg_qk_acc=dbg_t,
+                          v8=v8, v_scale=vs)
     torch.cuda.synchronize()
     return dict(q8=q8.cpu().numpy(), sq=sq.cpu().numpy(), k8=k8.cpu().numpy(),
                 sk=sk.cpu().numpy(), mask=u64(mask), out=out.float().cpu().numpy(),
                 lse=None if lse_t is None else lse_t.cpu().numpy(),
                 flags=None if flags_t is None else u64(flags_t),
-                dbg=None if dbg_t is None else dbg_t.cpu().numpy())
+                dbg=None if dbg_t is None else dbg_t.cpu().numpy(),
+                v8=None if v8 is None else v8.cpu().numpy(),
+                vs=None if vs is None else vs.cpu().numpy())
 
 
 def oracle_mask(cfg, S_q, S_k):
@@ -62,7 +69,7 @@ def oracle_mask(cfg, S_q, S_k):
                             f16, cfg.mask_seed, W)
 
 
-def oracle_problem(cfg, q, k, v, b=None, h=None, mask_words=None):
+def oracle_problem(cfg, q, k, v, b=None, h=None, mask_words=None, pv8=False):
     """Oracle Problem for all heads, or for the single query head (b, h) and
     its KV head (quantisation blocks never cross heads, so this is exact)."""
     S_q, S_k = q.shape[2], k.shape[2]
@@ -77,4 +84,4 @@ def oracle_problem(cfg, q, k, v, b=None, h=None, mask_words=None):
                           tile_n=cfg.tile_n, tiles_per_bit=cfg.tiles_per_bit,
                           frac_16bit=cfg.frac_16bit, seed=cfg.mask_seed, mask_words=mw,
                           sm_scale=cfg.sm_scale, adaptive=cfg.adaptive, exp8=cfg.exp8,
-                          tau=cfg.tau, sub_rows=cfg.sub_rows)
+                          tau=cfg.tau, sub_rows=cfg.sub_rows, pv8=pv8)

@@ -131,7 +131,7 @@ def test_library_exports_every_declared_symbol(lamp):
 
 
 def test_abi_version_and_status_strings(lamp):
-    assert lamp.lamp_abi_version() == 2
+    assert lamp.lamp_abi_version() == 3
     for i, n in enumerate(["LAMP_OK", "LAMP_ERR_NULL", "LAMP_ERR_SHAPE", "LAMP_ERR_UNSUPPORTED",
                            "LAMP_ERR_ALIGN", "LAMP_ERR_HIP"]):
         assert lamp.lamp_status_string(i) == n
@@ -191,6 +191,22 @@ def test_quantize_varlen_validation(lamp):
     assert f(p, 1, 1, 1, 64, 96, 0, 0, 96, None, 64, 2, p, p, None) == 3
     assert f(None, 1, 1, 1, 64, 128, 0, 0, 128, p, 64, 2, p, p, None) == 1
     assert f(None, 1, 1, 1, 0, 128, 0, 0, 128, p, 64, 2, None, None, None) == 0
+
+
+def test_quantize_v_tiles_validation(lamp):
+    f = _lib(lamp).lamp_quantize_v_tiles
+    p = ctypes.c_void_p(16)
+    assert f(p, 1, 1, 1, 64, 96, 0, 0, 96, None, p, p, None) == 3           # D
+    assert f(p, 2, 1, 1, 64, 128, 0, 0, 128, None, p, p, None) == 3         # v_dtype
+    assert f(p, 1, -1, 1, 64, 128, 0, 0, 128, None, p, p, None) == 2        # negative size
+    assert f(p, 1, 1, 1, 64, 128, 0, 0, -128, None, p, p, None) == 2        # negative stride
+    assert f(p, 1, 1, 1, 64, 128, 0, 0, 64, None, p, p, None) == 2          # stride < D
+    assert f(None, 1, 1, 1, 64, 128, 0, 0, 128, None, p, p, None) == 1
+    assert f(p, 1, 1, 1, 64, 128, 0, 0, 128, None, p, None, None) == 1
+    assert f(ctypes.c_void_p(18), 1, 1, 1, 64, 128, 0, 0, 128, None, p, p, None) == 4
+    assert f(p, 1, 1, 1, 64, 128, 0, 0, 132, None, p, p, None) == 4
+    assert f(p, 1, 1, 1, 64, 128, 0, 0, 128, ctypes.c_void_p(18), p, p, None) == 4
+    assert f(None, 1, 1, 1, 0, 128, 0, 0, 128, None, None, None, None) == 0
 
 
 def test_mask_template_validation(lamp):
@@ -258,6 +274,12 @@ def _params(lamp, **kw):
     (dict(causal=0, S_k=0), 2),
     (dict(seqlens_q=4098), 4),                   # lengths need 4-byte alignment
     (dict(seqlens_k=4097), 4),
+    (dict(pv8=2), 2),
+    (dict(pv8=1, v8=4096, v_scale=4096), 3),     # 8-bit P V needs exp8
+    (dict(pv8=1, exp8=1, mode=1, v8=4096, v_scale=4096), 3),   # and mask routing
+    (dict(pv8=1, exp8=1), 1),                    # V codes and scales required
+    (dict(pv8=1, exp8=1, v8=4100, v_scale=4096), 4),
+    (dict(pv8=1, exp8=1, v8=4096, v_scale=4098), 4),
     (dict(S_q=0, S_k=0), 0),                     # empty: OK, nothing launched
     (dict(B=0), 0),
 ])

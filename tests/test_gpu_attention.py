@@ -215,6 +215,42 @@ def test_small_lamp(case):
     assert rep.get("fragile_rows", 0) <= MAX_FRAGILE * rep["rows"]
 
 
+# 8-bit P V on 8-bit tiles (exp8, mask routing): e4m3 weights times
+# tile-packed e4m3 V with power-of-two block scales
+PV8 = [
+    # D, tm, dtype, code, causal, B, Hq, Hkv, S_q, S_k, G, f16
+    (128, 128, "bf16", "e4m3", True, 1, 2, 1, 320, 320, 1, 0.3),
+    (128, 128, "bf16", "i8", True, 2, 2, 1, 320, 320, 2, 0.3),
+    (64, 128, "f16", "e4m3", False, 1, 2, 1, 150, 260, 1, 0.3),
+    (256, 128, "bf16", "e4m3", True, 1, 2, 1, 256, 256, 1, 0.5),
+    (128, 64, "bf16", "i8", True, 1, 2, 2, 200, 200, 1, 0.2),
+    (128, 128, "bf16", "e4m3", True, 1, 4, 1, 777, 777, 1, 0.0),
+    (128, 128, "f16", "e4m3", True, 1, 2, 1, 200, 450, 1, 1.0),
+]
+
+
+@pytest.mark.parametrize("case", PV8, ids=lambda c: "d{}_m{}_{}_{}_c{}_s{}x{}_f{}".format(
+    c[0], c[1], c[2], c[3], int(c[4]), c[8], c[9], c[11]))
+def test_small_pv8(case):
+    D, tm, dt, code, causal, B, Hq, Hkv, S_q, S_k, G, f16 = case
+    cfg = small_cfg(D, tm, dt, code, causal, B, Hq, Hkv, max(S_q, S_k), G, f16, exp8=True)
+    if f16 == 0.0:
+        cfg = cfg.with_(mask_all_ones=True)
+    q, k, v = inputs_qk(cfg, S_q, S_k)
+    print(f"[attn] pv8 {case}", flush=True)
+    g = gpu_run(cfg, q, k, v, pv8=True)
+    P = oracle_problem(cfg, q, k, v, pv8=True)
+    check_codes_and_mask(cfg, P, g)
+    from oracle import quant as oq
+    assert (g["v8"] == oq.pack_v_tiles(P.v_codes)).all() and (g["vs"] == P.v_scales).all()
+    rep = {}
+    for b in range(B):
+        for h in range(Hq):
+            check_head(cfg, P, g, b, h, report=rep)
+    print(f"  pv8 report {rep}", flush=True)
+    assert rep.get("fragile_rows", 0) <= MAX_FRAGILE * rep["rows"]
+
+
 # ---------------------------------------------------------------------------
 # full-size configurations, sampled query tiles
 # ---------------------------------------------------------------------------

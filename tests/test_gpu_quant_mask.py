@@ -174,3 +174,55 @@ def test_mask_template_bit_exact(shape):
         torch.cuda.synchronize()
         ref = omask.build_mask_template(B, Hq, S_q, S_k, tm, tn, G, sink, band, stride, w)
         assert (m.cpu().numpy().view(np.uint64) == ref).all()
+
+
+# ---------------------------------------------------------------------------
+# V tiles for the 8-bit P V product
+# ---------------------------------------------------------------------------
+
+def assert_v_tiles_equal(v, seqlens=None):
+    sl = None if seqlens is None else torch.tensor(seqlens, dtype=torch.int32, device=dev())
+    gc, gs = L().lamp_quantize_v_tiles(v.to(dev()), seqlens=sl)
+    torch.cuda.synchronize()
+    gc, gs = gc.cpu().numpy(), gs.cpu().numpy()
+    oc, os_ = oq.quantize_v_tiles(v.float().numpy(), 64, seqlens)
+    assert (gs == os_).all(), f"scales differ at {np.argwhere(gs != os_)[:5]}"
+    packed = oq.pack_v_tiles(oc)
+    bad = np.argwhere(gc != packed)
+    assert bad.size == 0, f"{len(bad)} codes differ, first {bad[:5]}"
+
+
+@pytest.mark.parametrize("D,S,dtype,scale", [
+    (64, 200, torch.bfloat16, 1.0), (128, 320, torch.float16, 3.0), (256, 130, torch.bfloat16, 0.01),
+    (128, 64, torch.bfloat16, 1e4), (128, 1, torch.float16, 1.0)])
+def test_quant_v_tiles(D, S, dtype, scale):
+    g = torch.Generator().manual_seed(D + S)
+    v = (torch.randn(2, 3, S, D, generator=g) * scale).to(dtype)
+    v[1, 2, :40] = 0.0                                # an all-zero first tile (S >= 64 cases)
+    print(f"[quant v] D{D} S{S} {dtype} x{scale}", flush=True)
+    assert_v_tiles_equal(v)
+
+
+def test_quant_v_tiles_strided_and_varlen():
+    g = torch.Generator().manual_seed(5)
+    base = torch.randn(2, 300, 4, 128, generator=g).to(torch.bfloat16)
+    v = base.transpose(1, 2)                           # [2, 4, 300, 128], non-contiguous
+    print("[quant v] strided, varlen", flush=True)
+    assert_v_tiles_equal(v)
+    assert_v_tiles_equal(v, seqlens=[300, 97])
+    assert_v_tiles_equal(v, seqlens=[0, 64])
+
+
+def test_quant_v_tiles_rounding_midpoints():
+    # block absmax 448 -> scale 1, so the codes are the e4m3 rounding of the
+    # values themselves: midpoints must go to the even code
+    vals = crafted_e4m3_rows()
+    t = torch.tensor(vals, dtype=torch.float64).to(torch.bfloat16)
+    vals = vals[t.double().numpy() == vals]
+    n = len(vals) // 64 * 64
+    v = torch.tensor(vals[:n], dtype=torch.float64).to(torch.bfloat16).reshape(1, 1, n // 64, 64)
+    v = v.transpose(2, 3).contiguous()                 # [1, 1, 64, n/64]: pad D to 64
+    v = torch.nn.functional.pad(v, (0, 64 - v.shape[-1]))
+    v[0, 0, 0, 0] = 448.0
+    print("[quant v] midpoints", flush=True)
+    assert_v_tiles_equal(v)
