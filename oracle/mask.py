@@ -65,17 +65,27 @@ def n_tiles(S, tile):
 
 
 def group_bits(B, Hq, S_q, S_k, tile_m, tile_n, tiles_per_bit, frac_16bit, seed):
-    """bits[b, h, qt, g] (uint8, 1 = 8-bit path) of the random template."""
-    if not 0.0 <= frac_16bit <= 1.0:
+    """bits[b, h, qt, g] (uint8, 1 = 8-bit path) of the random template.
+
+    frac_16bit: one fraction for every head, or one per query head (a
+    sequence of Hq values: per-head mix ratios; the draws are the same, only
+    the threshold differs by head)."""
+    f = np.asarray(frac_16bit, dtype=np.float64)
+    if f.ndim == 0:
+        f = np.full(Hq, float(f))
+    if f.shape != (Hq,):
+        raise ValueError("frac_16bit: one value, or one per query head")
+    if not ((f >= 0.0) & (f <= 1.0)).all():
         raise ValueError("frac_16bit outside [0, 1]")
     n_qt = n_tiles(S_q, tile_m)
     n_kt = n_tiles(S_k, tile_n)
     n_g = n_tiles(n_kt, tiles_per_bit)
-    T = int(np.floor(frac_16bit * 4294967296.0))
+    # T = floor(f * 2^32) <= 2^32, compared with the upper 32 bits of the draw
+    T = np.array([int(np.floor(x * 4294967296.0)) for x in f], dtype=np.uint64)
     idx = np.arange(B * Hq * n_qt * n_g, dtype=np.uint64)
-    r = splitmix64(seed, idx)
-    is16 = (r >> np.uint64(32)) < np.uint64(T) if T < (1 << 32) else np.ones(idx.shape, bool)
-    return (~is16).astype(np.uint8).reshape(B, Hq, n_qt, n_g)
+    r = splitmix64(seed, idx).reshape(B, Hq, n_qt, n_g)
+    is16 = (r >> np.uint64(32)) < T[None, :, None, None]
+    return (~is16).astype(np.uint8)
 
 
 def pack_bits(bits, words_per_row):

@@ -35,10 +35,10 @@ def test_splitmix64_sequential_state():
 def brute_mask(B, Hq, S_q, S_k, tm, tn, G, f16, seed, W):
     n_qt, n_kt = -(-S_q // tm), -(-S_k // tn)
     n_g = -(-n_kt // G)
-    T = math.floor(f16 * 2 ** 32)
     out = np.zeros((B, Hq, n_qt, W), dtype=np.uint64)
     for b in range(B):
         for h in range(Hq):
+            T = math.floor((f16[h] if isinstance(f16, (list, tuple)) else f16) * 2 ** 32)
             for qt in range(n_qt):
                 words = [0] * W
                 for g in range(n_g):
@@ -60,6 +60,25 @@ def test_matches_brute_force(shape):
     B, Hq, S_q, S_k, tm, tn, G, f16, seed, W = shape
     got = mask.build_mask(B, Hq, S_q, S_k, tm, tn, G, f16, seed, W)
     assert (got == brute_mask(*shape)).all()
+
+
+@pytest.mark.parametrize("shape", [
+    (2, 4, 300, 300, 128, 64, 4, [0.0, 0.25, 0.9, 1.0], 17, 1),
+    (1, 3, 8192, 8192, 128, 64, 1, [0.1, 0.5, 0.3], 23, 2),
+])
+def test_per_head_matches_brute_force(shape):
+    B, Hq, S_q, S_k, tm, tn, G, f16, seed, W = shape
+    got = mask.build_mask(B, Hq, S_q, S_k, tm, tn, G, f16, seed, W)
+    assert (got == brute_mask(*shape)).all()
+
+
+def test_per_head_equal_fractions_is_scalar():
+    a = mask.build_mask(2, 5, 700, 700, 128, 64, 2, [0.3] * 5, 4, 1)
+    assert (a == mask.build_mask(2, 5, 700, 700, 128, 64, 2, 0.3, 4, 1)).all()
+    with pytest.raises(ValueError):
+        mask.group_bits(1, 3, 64, 64, 64, 64, 1, [0.1, 0.2], 1)
+    with pytest.raises(ValueError):
+        mask.group_bits(1, 2, 64, 64, 64, 64, 1, [0.1, 1.5], 1)
 
 
 def test_extremes_and_padding():
