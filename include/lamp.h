@@ -9,7 +9,8 @@
  *   8-bit path  Q and K quantised per block (int8 or OCP e4m3) with one fp32
  *               scale per block; 8-bit MFMA; logits rescaled by
  *               sQ * sK * sm_scale; optionally the max-shifted logit and its
- *               exponential rounded to e4m3 ("exp8").
+ *               exponential rounded to e4m3 ("exp8"); optionally, with exp8,
+ *               P V as an fp8 product with e4m3 V tiles ("pv8").
  *   16-bit path Q and K in bf16/fp16; 16-bit MFMA.
  *
  * Sources (pages, by title and section):
@@ -24,7 +25,8 @@
  *     identification of sensitive sub-blocks and their 16-bit recompute.
  *
  * Conventions for every entry point:
- *   - Every data pointer is a DEVICE pointer owned by the caller.  The
+ *   - Every data pointer is a DEVICE pointer owned by the caller (the one
+ *     exception, lamp_build_mask_per_head's fraction array, says so).  The
  *     library allocates no memory, keeps no state other than a thread-local
  *     error string, never synchronises, and enqueues its kernels on `stream`
  *     (a hipStream_t; NULL = the null stream).
@@ -162,6 +164,21 @@ lamp_status lamp_build_mask(int64_t B, int64_t Hq, int64_t S_q, int64_t S_k, int
                             int32_t tile_n, int32_t tiles_per_bit, double frac_16bit,
                             uint64_t seed, uint64_t* mask, int32_t words_per_row,
                             void* stream);
+
+/*
+ * lamp_build_mask_per_head -- lamp_build_mask with one 16-bit fraction per
+ * query head (per-head mix ratios; a per-layer ratio is one call per layer).
+ *
+ * Source: TileMix page, section 2 "Packed Bitmasks" (the mask policy is
+ * static and chosen per model).  frac_16bit: host array [Hq], each in
+ * [0, 1]; query head h uses the threshold floor(frac_16bit[h] * 2^32) with
+ * the same SplitMix64 draws as lamp_build_mask.  Hq <= 128.  Everything else
+ * as for lamp_build_mask.
+ */
+lamp_status lamp_build_mask_per_head(int64_t B, int64_t Hq, int64_t S_q, int64_t S_k,
+                                     int32_t tile_m, int32_t tile_n, int32_t tiles_per_bit,
+                                     const double* frac_16bit, uint64_t seed, uint64_t* mask,
+                                     int32_t words_per_row, void* stream);
 
 /*
  * lamp_build_mask_template -- a structured static packed precision mask.

@@ -7,7 +7,8 @@ loudly if it has not been built.
 """
 from .lamp import (  # noqa: F401
     LAMP_BF16, LAMP_E4M3, LAMP_F16, LAMP_I8, LAMP_MODE_ADAPTIVE, LAMP_MODE_MASK, LampError,
-    lamp_abi_version, lamp_attn_fwd, lamp_build_mask, lamp_build_mask_template, lamp_last_error,
+    lamp_abi_version, lamp_attn_fwd, lamp_build_mask, lamp_build_mask_per_head,
+    lamp_build_mask_template, lamp_last_error,
     lamp_quantize_blocks, lamp_quantize_v_tiles, lamp_decode_fwd, lamp_decode_workspace_bytes,
     lamp_status_string, library_path, exported_symbols,
 )

@@ -145,15 +145,30 @@ lamp_status lamp_quantize_v_tiles(const void* v, int32_t v_dtype, int64_t B, int
   return hip_status(lamp::launch_quantize_v(a, static_cast<hipStream_t>(stream)), "V quantize launch");
 }
 
-lamp_status lamp_build_mask(int64_t B, int64_t Hq, int64_t S_q, int64_t S_k, int32_t tile_m,
-                            int32_t tile_n, int32_t tiles_per_bit, double frac_16bit,
-                            uint64_t seed, uint64_t* mask, int32_t words_per_row,
-                            void* stream) {
+}  // extern "C"
+
+namespace {
+// floor(f * 2^32) in double, exact for every double f in [0, 1]
+uint64_t frac_threshold(double f) { return (uint64_t)std::floor(f * 4294967296.0); }
+
+lamp_status build_mask_common(int64_t B, int64_t Hq, int64_t S_q, int64_t S_k, int32_t tile_m,
+                              int32_t tile_n, int32_t tiles_per_bit, double frac_16bit,
+                              const double* frac_per_head, uint64_t seed, uint64_t* mask,
+                              int32_t words_per_row, void* stream) {
   if (B < 0 || Hq < 0 || S_q < 0 || S_k < 0) return fail(LAMP_ERR_SHAPE, "negative size");
   if (tile_m <= 0 || tile_n <= 0 || tiles_per_bit <= 0)
     return fail(LAMP_ERR_SHAPE, "tile sizes and tiles_per_bit must be positive");
-  if (!(frac_16bit >= 0.0 && frac_16bit <= 1.0))
+  if (frac_per_head) {
+    if (Hq > lamp::kMaskMaxHeads)
+      return fail(LAMP_ERR_UNSUPPORTED, "per-head fractions for Hq=%lld > %d heads", (long long)Hq,
+                  lamp::kMaskMaxHeads);
+    for (int64_t h = 0; h < Hq; ++h) {
+      if (!(frac_per_head[h] >= 0.0 && frac_per_head[h] <= 1.0))
+        return fail(LAMP_ERR_SHAPE, "frac_16bit[%lld] must lie in [0, 1]", (long long)h);
+    }
+  } else if (!(frac_16bit >= 0.0 && frac_16bit <= 1.0)) {
     return fail(LAMP_ERR_SHAPE, "frac_16bit must lie in [0, 1]");
+  }
   if (S_q > kMaxSeq || S_k > kMaxSeq) return fail(LAMP_ERR_UNSUPPORTED, "sequence too long");
   const int64_t n_qt = cdiv(S_q, tile_m), n_kt = cdiv(S_k, tile_n);
   const int64_t n_g = cdiv(n_kt, tiles_per_bit);
@@ -168,11 +183,36 @@ lamp_status lamp_build_mask(int64_t B, int64_t Hq, int64_t S_q, int64_t S_k, int
   a.total_words = B * Hq * n_qt * words_per_row;
   if (cdiv(a.total_words, 256) > kMaxGrid) return fail(LAMP_ERR_UNSUPPORTED, "mask too large");
   a.seed = seed;
-  // floor(f * 2^32) in double, exact for every double f in [0, 1]
-  a.threshold = (uint64_t)std::floor(frac_16bit * 4294967296.0);
+  a.threshold = frac_per_head ? 0 : frac_threshold(frac_16bit);
   a.words_per_row = words_per_row;
   a.n_g = (int32_t)n_g;
+  a.per_head = frac_per_head ? 1 : 0;
+  a.Hq = (int32_t)Hq;
+  a.n_qt = (int32_t)n_qt;
+  if (frac_per_head) {
+    for (int64_t h = 0; h < Hq; ++h) a.head_threshold[h] = frac_threshold(frac_per_head[h]);
+  }
   return hip_status(lamp::launch_build_mask(a, static_cast<hipStream_t>(stream)), "mask launch");
+}
+}  // namespace
+
+extern "C" {
+
+lamp_status lamp_build_mask(int64_t B, int64_t Hq, int64_t S_q, int64_t S_k, int32_t tile_m,
+                            int32_t tile_n, int32_t tiles_per_bit, double frac_16bit,
+                            uint64_t seed, uint64_t* mask, int32_t words_per_row,
+                            void* stream) {
+  return build_mask_common(B, Hq, S_q, S_k, tile_m, tile_n, tiles_per_bit, frac_16bit, nullptr,
+                           seed, mask, words_per_row, stream);
+}
+
+lamp_status lamp_build_mask_per_head(int64_t B, int64_t Hq, int64_t S_q, int64_t S_k,
+                                     int32_t tile_m, int32_t tile_n, int32_t tiles_per_bit,
+                                     const double* frac_16bit, uint64_t seed, uint64_t* mask,
+                                     int32_t words_per_row, void* stream) {
+  if (!frac_16bit && Hq > 0) return fail(LAMP_ERR_NULL, "frac_16bit is required");
+  return build_mask_common(B, Hq, S_q, S_k, tile_m, tile_n, tiles_per_bit, 0.0, frac_16bit, seed,
+                           mask, words_per_row, stream);
 }
 
 lamp_status lamp_build_mask_template(int64_t B, int64_t Hq, int64_t S_q, int64_t S_k,

@@ -29,6 +29,8 @@ struct VQuantArgs {
   bool bf16;
 };
 
+constexpr int kMaskMaxHeads = 128;      // per-head fractions ride in the kernel arguments
+
 struct MaskArgs {
   uint64_t* mask;
   int64_t total_words;         // B * Hq * n_qt * words_per_row
@@ -36,6 +38,9 @@ struct MaskArgs {
   uint64_t threshold;          // floor(frac_16bit * 2^32)
   int32_t words_per_row;
   int32_t n_g;
+  int32_t per_head;            // 1: threshold of query head h is head_threshold[h]
+  int32_t Hq, n_qt;
+  uint64_t head_threshold[kMaskMaxHeads];
 };
 
 struct TemplateMaskArgs {

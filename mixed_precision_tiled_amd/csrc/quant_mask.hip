@@ -213,13 +213,14 @@ __global__ __launch_bounds__(256) void build_mask_kernel(MaskArgs a) {
   if (wid >= a.total_words) return;
   const int64_t row = wid / a.words_per_row;        // (b*Hq + h)*n_qt + qt
   const int w = (int)(wid % a.words_per_row);
+  const uint64_t thr = a.per_head ? a.head_threshold[(row / a.n_qt) % a.Hq] : a.threshold;
   uint64_t word = 0;
   const int g0 = w * 64;
   const int gn = min(64, a.n_g - g0);
   for (int i = 0; i < gn; ++i) {
     const uint64_t idx = (uint64_t)row * (uint64_t)a.n_g + (uint64_t)(g0 + i);
     const uint64_t r = splitmix64(a.seed, idx);
-    const bool is16 = (r >> 32) < a.threshold;
+    const bool is16 = (r >> 32) < thr;
     word |= (uint64_t)(!is16) << i;
   }
   a.mask[wid] = word;

@@ -68,6 +68,9 @@ _lib.lamp_quantize_v_tiles.argtypes = [_vp, _i32, _i64, _i64, _i64, _i64, _i64, 
 _lib.lamp_build_mask.restype = _i32
 _lib.lamp_build_mask.argtypes = [_i64, _i64, _i64, _i64, _i32, _i32, _i32, ctypes.c_double, _u64,
                                  _vp, _i32, _vp]
+_lib.lamp_build_mask_per_head.restype = _i32
+_lib.lamp_build_mask_per_head.argtypes = [_i64, _i64, _i64, _i64, _i32, _i32, _i32,
+                                          ctypes.POINTER(ctypes.c_double), _u64, _vp, _i32, _vp]
 _lib.lamp_attn_fwd.restype = _i32
 _lib.lamp_build_mask_template.restype = _i32
 _lib.lamp_build_mask_template.argtypes = [_i64, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _i32,
@@ -193,6 +196,26 @@ def lamp_build_mask(B, Hq, S_q, S_k, tile_m, tile_n, tiles_per_bit, frac_16bit, 
         raise ValueError("mask must be contiguous")
     _check(_lib.lamp_build_mask(B, Hq, S_q, S_k, tile_m, tile_n, tiles_per_bit, float(frac_16bit),
                                 seed & ((1 << 64) - 1), _ptr(mask), W, _stream(mask)))
+    return mask
+
+
+def lamp_build_mask_per_head(B, Hq, S_q, S_k, tile_m, tile_n, tiles_per_bit, frac_16bit, seed,
+                             words_per_row=None, mask=None, device="cuda"):
+    """Random packed mask with one 16-bit fraction per query head
+    (frac_16bit: Hq floats), int64 tensor [B, Hq, n_qt, W]."""
+    n_qt = cdiv(S_q, tile_m)
+    n_g = cdiv(cdiv(S_k, tile_n), tiles_per_bit)
+    W = words_per_row or max(1, cdiv(n_g, 64))
+    fr = [float(x) for x in frac_16bit]
+    if len(fr) != Hq:
+        raise ValueError("one fraction per query head")
+    if mask is None:
+        mask = torch.empty((B, Hq, n_qt, W), dtype=torch.int64, device=device)
+    if not mask.is_contiguous():
+        raise ValueError("mask must be contiguous")
+    arr = (ctypes.c_double * max(1, Hq))(*fr)
+    _check(_lib.lamp_build_mask_per_head(B, Hq, S_q, S_k, tile_m, tile_n, tiles_per_bit, arr,
+                                         seed & ((1 << 64) - 1), _ptr(mask), W, _stream(mask)))
     return mask
 
 

@@ -182,6 +182,24 @@ def test_mask_validation(lamp):
     assert f(0, 1, 256, 256, 64, 64, 1, 0.5, 0, None, 1, None) == 0
 
 
+def test_mask_per_head_validation(lamp):
+    f = _lib(lamp).lamp_build_mask_per_head
+    p = ctypes.c_void_p(64)
+    fr = (ctypes.c_double * 3)(0.1, 0.5, 1.0)
+    bad = (ctypes.c_double * 3)(0.1, 1.5, 0.2)
+    nan = (ctypes.c_double * 3)(0.1, float("nan"), 0.2)
+    big = (ctypes.c_double * 129)(*([0.5] * 129))
+    assert f(1, 3, 256, 256, 64, 64, 1, None, 0, p, 1, None) == 1
+    assert f(1, 3, 256, 256, 64, 64, 1, bad, 0, p, 1, None) == 2
+    assert f(1, 3, 256, 256, 64, 64, 1, nan, 0, p, 1, None) == 2
+    assert "frac_16bit[1]" in lamp.lamp_last_error()
+    assert f(1, 129, 256, 256, 64, 64, 1, big, 0, p, 1, None) == 3
+    assert f(1, 3, 8192, 8192, 128, 64, 1, fr, 0, p, 1, None) == 3     # words_per_row
+    assert f(1, 3, 256, 256, 64, 64, 1, fr, 0, None, 1, None) == 1
+    assert f(1, 3, 256, 256, 64, 64, 1, fr, 0, ctypes.c_void_p(65), 1, None) == 4
+    assert f(0, 3, 256, 256, 64, 64, 1, fr, 0, None, 1, None) == 0
+
+
 def test_quantize_varlen_validation(lamp):
     f = _lib(lamp).lamp_quantize_blocks_varlen
     p = ctypes.c_void_p(16)

@@ -156,6 +156,21 @@ def test_mask_bit_exact(shape):
 
 
 @pytest.mark.parametrize("shape", [
+    (1, 4, 512, 512, 64, 64, 1, [0.0, 0.3, 0.7, 1.0], 31),
+    (2, 32, 16384, 16384, 128, 64, 4, [0.05 * (h % 8) for h in range(32)], 2025),
+    (1, 3, 8192, 8192, 128, 64, 1, [0.2, 0.5, 0.25], 41),        # two words
+])
+def test_mask_per_head_bit_exact(shape):
+    B, Hq, S_q, S_k, tm, tn, G, fr, seed = shape
+    n_g = -(-(-(-S_k // tn)) // G)
+    W = max(1, -(-n_g // 64))
+    m = L().lamp_build_mask_per_head(B, Hq, S_q, S_k, tm, tn, G, fr, seed, W, device=dev())
+    torch.cuda.synchronize()
+    ref = omask.build_mask(B, Hq, S_q, S_k, tm, tn, G, fr, seed, W)
+    assert (m.cpu().numpy().view(np.uint64) == ref).all()
+
+
+@pytest.mark.parametrize("shape", [
     (1, 1, 512, 512, 64, 64, 1, 1, 2, 3),
     (2, 32, 16384, 16384, 128, 64, 4, 1, 2, 8),
     (1, 4, 8192, 8192, 128, 64, 1, 2, 3, 16),      # 128 groups: two words
