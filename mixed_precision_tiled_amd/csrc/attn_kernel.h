@@ -140,6 +140,9 @@ void attn_fwd_kernel(const AttnArgs a) {
   if (qt * SH::TM >= Lq) return;
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  // the wave index as a scalar, for the LDS destinations of the tile copies
+  // (M0), so that they need no per-copy lane read
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   const int lr = lane & 31, hf = lane >> 5;
   const int row0 = qt * SH::TM + w * 32;
   const int my_row = row0 + lr;
@@ -186,9 +189,22 @@ void attn_fwd_kernel(const AttnArgs a) {
   const uint32_t kss = 2u * (uint32_t)a.k_ss, vss = 2u * (uint32_t)a.v_ss;
   const int key_max = Lk - 1;
 
-  auto tile_is8 = [&](int kt) -> bool {
-    const int g = kt / a.tiles_per_bit;
-    return (ld_uniform(mrow + (g >> 6)) >> (g & 63)) & 1ull;
+  // Mask bits of tiles 0, 1, 2, ... in order: the row's current mask word
+  // stays in registers (reloaded when the group index enters the next word)
+  // and the group index advances with a counter, so a step needs neither a
+  // division nor a memory load to route its next tile.
+  int rt_g = 0, rt_r = 0, rt_w = 0;
+  uint64_t rt_word = ld_uniform(mrow);
+  auto next_tile_is8 = [&]() -> bool {
+    if (++rt_r == a.tiles_per_bit) {
+      rt_r = 0;
+      ++rt_g;
+      if ((rt_g >> 6) != rt_w) {
+        rt_w = rt_g >> 6;
+        rt_word = ld_uniform(mrow + rt_w);
+      }
+    }
+    return (rt_word >> (rt_g & 63)) & 1ull;
   };
 
   // ---- direct-to-LDS staging of one key tile.  Wave w issues copies
@@ -239,21 +255,31 @@ void attn_fwd_kernel(const AttnArgs a) {
   const uint32_t k16_bytes = Lk > 0 ? (uint32_t)(Lk - 1) * kss + 2u * D : 0u;
   const uint32_t k8_bytes = (uint32_t)Lk * D;
   const uint32_t v_bytes = Lk > 0 ? (uint32_t)(Lk - 1) * vss + 2u * D : 0u;
+  // per-step copy of the scalar wave index: the copies' LDS addresses are
+  // then a few scalar adds per step instead of registers held (and spilled)
+  // across the loop
+  auto wave_s = [&]() {
+    int v = wu;
+    asm volatile("" : "+s"(v));
+    return v;
+  };
   auto issue_k = [&](int kt, bool is8, char* kdst) {
+    const int wu = wave_s();
     const uint32_t key0 = (uint32_t)(kt * SH::TN);
     if (is8) {
       const auto rs = make_rsrc(k8base + key0 * D, k8_bytes - key0 * D);
 #pragma unroll
       for (int j = 0; j < SH::JK8; ++j)
-        dma16_buf(rs, copy_off(off_k8, K8_1, j, (uint32_t)(RS8 * D)), 0u, kdst + 1024 * (w + NW * j));
+        dma16_buf(rs, copy_off(off_k8, K8_1, j, (uint32_t)(RS8 * D)), 0u, kdst + 1024 * (wu + NW * j));
     } else {
       const auto rs = make_rsrc(kbase + key0 * kss, k16_bytes - key0 * kss);
 #pragma unroll
       for (int j = 0; j < SH::JK16; ++j)
-        dma16_buf(rs, copy_off(off_k16, K16_1, j, (uint32_t)RS16 * kss), 0u, kdst + 1024 * (w + NW * j));
+        dma16_buf(rs, copy_off(off_k16, K16_1, j, (uint32_t)RS16 * kss), 0u, kdst + 1024 * (wu + NW * j));
     }
   };
   auto issue_v = [&](int kt, bool is8, char* vdst) {
+    const int wu = wave_s();
     if constexpr (PV8) {
       if (is8) {
         // whole tiles, always in bounds (the quantiser zero-fills keys past
@@ -261,7 +287,7 @@ void attn_fwd_kernel(const AttnArgs a) {
         const uint8_t* src = v8base + (int64_t)kt * SH::V8_BYTES;
 #pragma unroll
         for (int j = 0; j < SH::JV8; ++j)
-          dma16(src + 1024 * (w + NW * j) + off_v8, vdst + 1024 * (w + NW * j));
+          dma16(src + 1024 * (wu + NW * j) + off_v8, vdst + 1024 * (wu + NW * j));
         return;
       }
     }
@@ -269,7 +295,7 @@ void attn_fwd_kernel(const AttnArgs a) {
     const auto rv = make_rsrc(vbase + key0 * vss, v_bytes - key0 * vss);
 #pragma unroll
     for (int j = 0; j < SH::JV; ++j)
-      dma16_buf(rv, copy_off(off_v, V_1, j, (uint32_t)RS16 * vss), 0u, vdst + 1024 * (w + NW * j));
+      dma16_buf(rv, copy_off(off_v, V_1, j, (uint32_t)RS16 * vss), 0u, vdst + 1024 * (wu + NW * j));
   };
 
   // ---- per-lane LDS read offsets ----
@@ -645,8 +671,11 @@ void attn_fwd_kernel(const AttnArgs a) {
   uint32_t pk[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) pk[i] = 0u;
-  bool is8_cur = tile_is8(0);
+  bool is8_cur = rt_word & 1ull;
+  // sK of the current tile and the next one; a step loads the one after
+  // that, a step ahead of its use
   float sk_cur = ld_uniform(sKp);
+  float sk_n1 = a.n_kt > 1 ? ld_uniform(sKp + 1) : 0.f;
   // route and V scale (E8M0 code) of the tile whose P V is pending
   bool is8_prev = false;
   int svc_cur = 127, svc_prev = 127;
@@ -673,12 +702,11 @@ void attn_fwd_kernel(const AttnArgs a) {
   auto step = [&](auto first, int kt, const char* kcur, char* knxt, const char* vprev, char* vcur) {
     constexpr bool FIRST = decltype(first)::value;
     bool is8_next = false;
-    float sk_next = 0.f;
-    if (kt + 1 < kt_end) {
-      is8_next = tile_is8(kt + 1);
-      sk_next = ld_uniform(sKp + kt + 1);
-      issue_k(kt + 1, is8_next, knxt);
-    }
+    if (kt + 1 < kt_end) is8_next = next_tile_is8();
+    // (after the mask bit, so that a wait for a reloaded mask word does not
+    // also wait for this load)
+    const float sk_n2 = kt + 2 < kt_end ? ld_uniform(sKp + kt + 2) : 0.f;
+    if (kt + 1 < kt_end) issue_k(kt + 1, is8_next, knxt);
     if constexpr (PV8) {
       if (is8_cur) svc_cur = (int)((__builtin_bit_cast(uint32_t, ld_uniform(sVp + kt)) >> 23) & 0xFFu);
     }
@@ -717,7 +745,8 @@ void attn_fwd_kernel(const AttnArgs a) {
     is8_prev = is8_cur;
     svc_prev = svc_cur;
     is8_cur = is8_next;
-    sk_cur = sk_next;
+    sk_cur = sk_n1;
+    sk_n1 = sk_n2;
   };
   if (kt_end > 0) step(True_{}, 0, sk0, sk1, sv1, sv0);
   for (int kt = 1; kt < kt_end; kt += 2) {
