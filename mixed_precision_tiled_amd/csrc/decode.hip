@@ -13,7 +13,8 @@
 //   * decode_split_kernel: one wave per (b, kv head, split of 512 keys); the
 //     group's queries (heads_per_group x S_q <= 32 columns) are the B operand
 //     of int8 32x32x32 MFMAs (S^T = K8 Q8^T, K8 straight from global memory
-//     into registers, each byte read once); online softmax per column; V
+//     into registers, each byte read once, the next tile's codes loaded while
+//     the current one is computed); online softmax per column; V
 //     codes are converted to 16 bits into LDS in the prefill kernel's layout
 //     and multiplied as O^T += V^T P^T, with sV folded into P.  Each wave
 //     writes its unnormalised partial (m, l, O) to the caller's workspace;
@@ -78,26 +79,34 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   const float c_log = a.sm_scale * kLog2e * sQ;
 
   const int kt0 = split * kTilesPerSplit, kt1 = min(a.n_kt, kt0 + kTilesPerSplit);
-  for (int kt = kt0; kt < kt1; ++kt) {
-    const int key0 = kt * SH::TN;
-    // K codes, A operand: rows key0 + 32 kb + lr (clamped; masked below)
+  // One tile's codes in registers: K as the A operand (rows key0 + 32 kb +
+  // lr, clamped; masked below) and V one key row per lane.  The loads of
+  // tile kt+1 are issued before tile kt is computed, so a wave always has a
+  // tile in flight while it computes.
+  struct TileCodes {
     u32x4 kf0[SH::NQ8], kf1[SH::NQ8];
-    {
-      const uint8_t* p0 = k8base + (int64_t)min(key0 + lr, a.S_k - 1) * D + 16 * hf;
-      const uint8_t* p1 = k8base + (int64_t)min(key0 + 32 + lr, a.S_k - 1) * D + 16 * hf;
-#pragma unroll
-      for (int t = 0; t < SH::NQ8; ++t) {
-        kf0[t] = ld_global16(p0 + 32 * t);
-        kf1[t] = ld_global16(p1 + 32 * t);
-      }
-    }
-    // V codes: one key row per lane
     u32x4 vcode[D / 16];
-    {
-      const uint8_t* pv = v8base + (int64_t)min(key0 + lane, a.S_k - 1) * D;
+  };
+  auto load_tile = [&](int kt, TileCodes& tc) {
+    const int key0 = kt * SH::TN;
+    const uint8_t* p0 = k8base + (int64_t)min(key0 + lr, a.S_k - 1) * D + 16 * hf;
+    const uint8_t* p1 = k8base + (int64_t)min(key0 + 32 + lr, a.S_k - 1) * D + 16 * hf;
 #pragma unroll
-      for (int c = 0; c < D / 16; ++c) vcode[c] = ld_global16(pv + 16 * c);
+    for (int t = 0; t < SH::NQ8; ++t) {
+      tc.kf0[t] = ld_global16(p0 + 32 * t);
+      tc.kf1[t] = ld_global16(p1 + 32 * t);
     }
+    const uint8_t* pv = v8base + (int64_t)min(key0 + lane, a.S_k - 1) * D;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) tc.vcode[c] = ld_global16(pv + 16 * c);
+    // keep the loads here, ahead of the computation they overlap
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto compute_tile = [&](int kt, const TileCodes& tc) {
+    const int key0 = kt * SH::TN;
+    const u32x4* kf0 = tc.kf0;
+    const u32x4* kf1 = tc.kf1;
+    const u32x4* vcode = tc.vcode;
     const float sK = ld_uniform(sKp + kt), sV = ld_uniform(sVp + kt);
 
     // logits (base 2) of the 64 keys x 32 columns
@@ -171,6 +180,21 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
           O[db] = mfma16<BF16>(u32x4{lo.x, lo.y, hi.x, hi.y}, pb, O[db]);
         }
       }
+    }
+  };
+  // two register sets, alternating (unrolled by two so that each names its
+  // set statically): one tile in flight while the other is computed.  The
+  // prefetch is unconditional (past the split's last tile it reloads that
+  // tile, an L2 hit): conditional loads would make the wait for the current
+  // set count every load in flight.
+  TileCodes ta, tb;
+  if (kt0 < kt1) load_tile(kt0, ta);
+  for (int kt = kt0; kt < kt1; kt += 2) {
+    load_tile(min(kt + 1, kt1 - 1), tb);
+    compute_tile(kt, ta);
+    if (kt + 1 < kt1) {
+      load_tile(min(kt + 2, kt1 - 1), ta);
+      compute_tile(kt + 1, tb);
     }
   }
 
