@@ -10,11 +10,11 @@
 //
 // Decode is bound by reading the cache from HBM (2 D bytes per key, once).
 // Split-K over the keys:
-//   * decode_split_kernel: one wave per (b, kv head, split of 512 keys); the
+//   * decode_split_kernel: one wave per (b, kv head, split of 2048 keys); the
 //     group's queries (heads_per_group x S_q <= 32 columns) are the B operand
 //     of int8 32x32x32 MFMAs (S^T = K8 Q8^T, K8 straight from global memory
-//     into registers, each byte read once, the next tile's codes loaded while
-//     the current one is computed); online softmax per column; V
+//     into registers, each byte read once, three tiles' codes in flight
+//     while one is computed); online softmax per column; V
 //     codes are converted to 16 bits into LDS in the prefill kernel's layout
 //     and multiplied as O^T += V^T P^T, with sV folded into P.  Each wave
 //     writes its unnormalised partial (m, l, O) to the caller's workspace;
@@ -182,20 +182,26 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       }
     }
   };
-  // two register sets, alternating (unrolled by two so that each names its
-  // set statically): one tile in flight while the other is computed.  The
-  // prefetch is unconditional (past the split's last tile it reloads that
-  // tile, an L2 hit): conditional loads would make the wait for the current
-  // set count every load in flight.
-  TileCodes ta, tb;
-  if (kt0 < kt1) load_tile(kt0, ta);
-  for (int kt = kt0; kt < kt1; kt += 2) {
-    load_tile(min(kt + 1, kt1 - 1), tb);
-    compute_tile(kt, ta);
-    if (kt + 1 < kt1) {
-      load_tile(min(kt + 2, kt1 - 1), ta);
-      compute_tile(kt + 1, tb);
-    }
+  // four register sets in a ring (unrolled by four so that each names its
+  // set statically): three tiles in flight while one is computed.  The
+  // prefetches are unconditional (past the split's last tile they reload
+  // that tile, an L2 hit): conditional loads would make the wait for the
+  // current set count every load in flight.
+  TileCodes t0, t1, t2, t3;
+  if (kt0 < kt1) {
+    load_tile(kt0, t0);
+    load_tile(min(kt0 + 1, kt1 - 1), t1);
+    load_tile(min(kt0 + 2, kt1 - 1), t2);
+  }
+  for (int kt = kt0; kt < kt1; kt += 4) {
+    load_tile(min(kt + 3, kt1 - 1), t3);
+    compute_tile(kt, t0);
+    load_tile(min(kt + 4, kt1 - 1), t0);
+    if (kt + 1 < kt1) compute_tile(kt + 1, t1);
+    load_tile(min(kt + 5, kt1 - 1), t1);
+    if (kt + 2 < kt1) compute_tile(kt + 2, t2);
+    load_tile(min(kt + 6, kt1 - 1), t2);
+    if (kt + 3 < kt1) compute_tile(kt + 3, t3);
   }
 
   // partial of this split: O^T block db holds rows d = 32 db + 8 (r / 4) +

@@ -85,9 +85,11 @@ struct AttnArgs {
   float tau;
 };
 
-// Decode over an int8 key/value cache: 64-key tiles per split of the keys
-constexpr int kDecodeTilesPerSplit = 8;
-constexpr int kMergeMaxSplit = 4096;     // splits of one merge (S_k <= 2^20 / 512 keys)
+// Decode over an int8 key/value cache: 64-key tiles per split of the keys (2048
+// keys: one round of one wave per SIMD at Qwen3-8B-like shapes, the ring of
+// register sets in each wave keeping three tiles of loads in flight)
+constexpr int kDecodeTilesPerSplit = 32;
+constexpr int kMergeMaxSplit = 4096;     // splits of one merge (S_k <= 2^20 keys: at most 512)
 
 struct DecodeArgs {
   const uint8_t* q8;
