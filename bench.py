@@ -364,6 +364,37 @@ class Pipeline:
                             self.cfg.tiles_per_bit, self.cfg.causal, fl, ls, ls)
 
 
+def other_workloads(torch, L):
+    """Attention alone on the 32k-token int8 workload (f = 0.10) and on the
+    adaptive e4m3 workload with 8-bit exponentials (head dim 256, outlier
+    channels and a sink key), each against its mix-weighted roofline (the
+    adaptive one counting its flagged recompute)."""
+    from synthetic import get_config, make_inputs
+    dev = torch.device("cuda:0")
+    out = {}
+    for name in ("C4", "C3"):
+        cfg = get_config(name)
+        q, k, v = make_inputs(cfg)
+        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+        del q, k, v
+        sp = Pipeline(L, cfg, qd, kd, vd, torch)
+        sp.prep()
+        ts = time_attn(torch, sp, iters=5, warmup=1)
+        cc = sp.counts()
+        tr = roofline_time(cc, cfg.D)
+        med = float(np.median(ts))
+        rec = {"workload": cfg.name, "attn_ms": round(med * 1e3, 4),
+               "tflops": round(algorithmic_flops(cc, cfg.D) / med / 1e12, 1),
+               "roofline_frac": round(tr / med, 4), "t_roof_ms": round(tr * 1e3, 4),
+               "fa_convention_tflops": round(cfg.fa_flops() / med / 1e12, 1)}
+        if cfg.adaptive:
+            rec["flagged_frac_of_8bit"] = round(cc["nflag"] / max(1, cc["n8"]), 4)
+        out[name] = rec
+        del sp, qd, kd, vd
+        torch.cuda.empty_cache()
+    return out
+
+
 def time_attn(torch, pipe, iters, warmup):
     for _ in range(warmup):
         pipe.attn()
@@ -550,6 +581,9 @@ def main():
         dm = decode_measurement(torch, L)
         result["decode_int8_kv"] = dm
         log(f"[bench] decode over an int8 K/V cache: {json.dumps(dm)}")
+        ow = other_workloads(torch, L)
+        result["other_workloads"] = ow
+        log(f"[bench] other workloads: {json.dumps(ow)}")
     if not args.no_cpu:
         log("[bench] timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(cfg, q, k, v, budget_s=args.cpu_budget)
