@@ -28,7 +28,11 @@
 //     step computes the logits of tile kt and interleaves P V of tile kt-1
 //     with the softmax arithmetic of tile kt;
 //   * workgroups are mapped so that each XCD processes whole KV-head groups
-//     (shared K/V in its L2), longest causal query tiles first.
+//     (shared K/V in its L2), longest causal query tiles first;
+//   * optional 8-bit P V (with 8-bit exponentials under mask routing): an
+//     8-bit tile stages its tile-packed e4m3 V block and multiplies it with
+//     the e4m3 weights in fp8 MFMAs, the V tile's power-of-two scale as the
+//     operand's block scale.
 #pragma once
 
 #include <type_traits>
