@@ -397,15 +397,19 @@ VARLEN = [
      False, False),
     (256, 128, "bf16", "i8", True, 2, 1, 260, 400, 1, 0.5, [260, 5], [400, 130], False, False),
     (128, 128, "bf16", "e4m3", True, 2, 1, 300, 300, 1, 0.3, [300, 130], [300, 290], True, True),
+    # with the 8-bit P V (V tiles quantised with the same lengths)
+    (128, 128, "bf16", "i8", True, 2, 1, 300, 300, 1, 0.3, [300, 130], [300, 290], True, False,
+     True),
 ]
 
 
-@pytest.mark.parametrize("case", VARLEN, ids=lambda c: "d{}_m{}_{}_{}_{}_Lq{}_Lk{}_x8{}_ad{}".format(
+@pytest.mark.parametrize("case", VARLEN, ids=lambda c: "d{}_m{}_{}_{}_{}_Lq{}_Lk{}_x8{}_ad{}{}".format(
     c[0], c[1], c[2], c[3], "causal" if c[4] else "full", "-".join(map(str, c[11])),
-    "-".join(map(str, c[12])), int(c[13]), int(c[14])))
+    "-".join(map(str, c[12])), int(c[13]), int(c[14]), "_pv8" if len(c) > 15 and c[15] else ""))
 def test_varlen(case):
     import mixed_precision_tiled_amd as L
-    D, tm, dt, code, causal, Hq, Hkv, S_q, S_k, G, f16, Lq, Lk, exp8, ad = case
+    D, tm, dt, code, causal, Hq, Hkv, S_q, S_k, G, f16, Lq, Lk, exp8, ad = case[:15]
+    pv8 = len(case) > 15 and case[15]
     B = len(Lq)
     cfg = small_cfg(D, tm, dt, code, causal, B, Hq, Hkv, max(S_q, S_k), G, f16, exp8=exp8,
                     adaptive=ad)
@@ -429,18 +433,25 @@ def test_varlen(case):
     flags = None
     if ad:
         flags = torch.full(L.lamp.flags_shape(B, Hq, S_q, S_k), -1, dtype=torch.int64, device=dev)
+    v8 = vs = None
+    if pv8:
+        v8, vs = L.lamp_quantize_v_tiles(vd, seqlens=lk)
     out = L.lamp_attn_fwd(qd, kd, vd, q8, k8, sq, sk, mask, code=code, causal=causal,
                           tile_m=tm, tiles_per_bit=G,
                           mode=L.LAMP_MODE_ADAPTIVE if ad else L.LAMP_MODE_MASK, exp8=exp8,
                           tau=cfg.tau, sub_rows=32, lse=lse, flags_out=flags,
-                          seqlens_q=lq, seqlens_k=lk)
+                          seqlens_q=lq, seqlens_k=lk, v8=v8, v_scale=vs)
     torch.cuda.synchronize()
     P = A.make_problem(q0.double().numpy(), k0.double().numpy(), v0.double().numpy(),
                        causal=causal, code=code, tile_m=tm, tile_n=64, tiles_per_bit=G,
                        frac_16bit=f16, seed=cfg.mask_seed, words_per_row=W,
                        seqlens_q=np.array(Lq), seqlens_k=np.array(Lk), adaptive=ad, exp8=exp8,
-                       tau=cfg.tau, sub_rows=32)
+                       tau=cfg.tau, sub_rows=32, pv8=pv8)
     assert (q8.cpu().numpy() == P.q_codes).all() and (sq.cpu().numpy() == P.q_scales).all()
+    if pv8:
+        from oracle import quant as oq
+        assert (v8.cpu().numpy() == oq.pack_v_tiles(P.v_codes)).all()
+        assert (vs.cpu().numpy() == P.v_scales).all()
     assert (k8.cpu().numpy() == P.k_codes).all() and (sk.cpu().numpy() == P.k_scales).all()
     got, glse = out.float().cpu().numpy(), lse.cpu().numpy()
     gflags = None if flags is None else u64(flags)
