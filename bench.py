@@ -422,17 +422,23 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the run, copy MIB MiB device-to-device once (reference "
                          "dispatch for scaling the HBM byte counters)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the decode measurement over an int8 K/V cache (for profiling)")
     args = ap.parse_args()
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              f"(each (batch, KV head) group is independent, see the design notes on sharding)",
-              file=sys.stderr)
+              f"(each (batch, KV head) group is independent: the path would shard by KV head "
+              f"with no exchange)", file=sys.stderr)
         sys.exit(2)
 
     import torch
     import mixed_precision_tiled_amd as L
     from synthetic import C5_FRACS, get_config, make_inputs
+
+    if args.decode_only:
+        print(json.dumps({"decode_int8_kv": decode_measurement(torch, L)}), flush=True)
+        return
 
     cfg = get_config(args.config, args.frac, args.code)
     if args.config == "C5" and args.frac is None and args.code is None:
