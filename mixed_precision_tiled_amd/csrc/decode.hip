@@ -10,7 +10,8 @@
 //
 // Decode is bound by reading the cache from HBM (2 D bytes per key, once).
 // Split-K over the keys:
-//   * decode_split_kernel: one wave per (b, kv head, split of 2048 keys); the
+//   * decode_split_kernel: one wave per (b, kv head, split of 512 to 2048 keys,
+//     sized to give the grid about one wave per SIMD); the
 //     group's queries (heads_per_group x S_q <= 32 columns) are the B operand
 //     of int8 32x32x32 MFMAs (S^T = K8 Q8^T, K8 straight from global memory
 //     into registers, each byte read once, three tiles' codes in flight
@@ -27,7 +28,6 @@ namespace lamp {
 
 namespace {
 
-constexpr int kTilesPerSplit = kDecodeTilesPerSplit;
 constexpr int kMergeThreads = 128;
 
 template <int D, bool BF16>
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   float m_run = kNegInf, l_run = 0.f;
   const float c_log = a.sm_scale * kLog2e * sQ;
 
-  const int kt0 = split * kTilesPerSplit, kt1 = min(a.n_kt, kt0 + kTilesPerSplit);
+  const int kt0 = split * a.tiles_per_split, kt1 = min(a.n_kt, kt0 + a.tiles_per_split);
   // One tile's codes in registers: K as the A operand (rows key0 + 32 kb +
   // lr, clamped; masked below) and V one key row per lane.  The loads of
   // tile kt+1 are issued before tile kt is computed, so a wave always has a

@@ -395,7 +395,8 @@ lamp_status lamp_attn_fwd(const lamp_attn_params* p, void* stream) {
 
 size_t lamp_decode_workspace_bytes(int64_t B, int64_t Hkv, int64_t S_k, int64_t D) {
   if (B < 0 || Hkv < 0 || S_k < 0 || D < 0) return 0;
-  const int64_t n_split = cdiv(cdiv(S_k, 64), lamp::kDecodeTilesPerSplit);
+  const int64_t n_kt = cdiv(S_k, 64);
+  const int64_t n_split = cdiv(n_kt, lamp::decode_tiles_per_split(B, Hkv, n_kt));
   return (size_t)(B * Hkv * n_split * 32 * (D + 2) * (int64_t)sizeof(float));
 }
 
@@ -451,7 +452,8 @@ lamp_status lamp_decode_fwd(const lamp_decode_params* p, void* workspace, size_t
   a.tile_m = p->tile_m;
   a.n_qt = (int32_t)cdiv(p->S_q, p->tile_m);
   a.n_kt = (int32_t)cdiv(p->S_k, 64);
-  a.n_split = (int32_t)cdiv(a.n_kt, lamp::kDecodeTilesPerSplit);
+  a.tiles_per_split = lamp::decode_tiles_per_split(a.B, a.Hkv, a.n_kt);
+  a.n_split = (int32_t)cdiv(a.n_kt, a.tiles_per_split);
   if ((int64_t)a.B * a.Hkv * a.n_split > kMaxGrid || a.n_split > lamp::kMergeMaxSplit)
     return fail(LAMP_ERR_UNSUPPORTED, "grid too large");
   a.o_sb = p->o_str[0];

@@ -85,11 +85,20 @@ struct AttnArgs {
   float tau;
 };
 
-// Decode over an int8 key/value cache: 64-key tiles per split of the keys (2048
-// keys: one round of one wave per SIMD at Qwen3-8B-like shapes, the ring of
-// register sets in each wave keeping three tiles of loads in flight)
-constexpr int kDecodeTilesPerSplit = 32;
-constexpr int kMergeMaxSplit = 4096;     // splits of one merge (S_k <= 2^20 keys: at most 512)
+// Decode over an int8 key/value cache: 64-key tiles per split of the keys.
+// The split length aims at one wave per SIMD over the whole grid (1024
+// SIMDs), within [8, 32] tiles: long enough for the ring of register sets in
+// each wave (three tiles of loads in flight) to pay off, short enough to fill
+// the chip at small batch.
+constexpr int kDecodeMinTilesPerSplit = 8;
+constexpr int kDecodeMaxTilesPerSplit = 32;
+constexpr int64_t kDecodeTargetWaves = 1024;
+inline int decode_tiles_per_split(int64_t B, int64_t Hkv, int64_t n_kt) {
+  const int64_t want = (B * Hkv * n_kt + kDecodeTargetWaves - 1) / kDecodeTargetWaves;
+  return (int)(want < kDecodeMinTilesPerSplit ? kDecodeMinTilesPerSplit
+                                              : want > kDecodeMaxTilesPerSplit ? kDecodeMaxTilesPerSplit : want);
+}
+constexpr int kMergeMaxSplit = 4096;     // splits of one merge (S_k <= 2^20 keys: at most 2048)
 
 struct DecodeArgs {
   const uint8_t* q8;
@@ -105,7 +114,7 @@ struct DecodeArgs {
   int64_t o_sb, o_sh, o_ss;
   int32_t B, Hq, Hkv, S_q, S_k, D;
   int32_t hpg, cols;           // Hq / Hkv, hpg * S_q (<= 32)
-  int32_t tile_m, n_qt, n_kt, n_split;
+  int32_t tile_m, n_qt, n_kt, n_split, tiles_per_split;
   int32_t causal;
   float sm_scale;
   bool bf16;

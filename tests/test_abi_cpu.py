@@ -104,8 +104,8 @@ def test_decode_validation(lamp):
             setattr(p, key, val)
         return p
     need = lamp.lamp_decode_workspace_bytes(1, 2, 1000, 128)
-    # splits of 2048 keys (32 tiles): 1000 keys are one split
-    assert need == 1 * 2 * 1 * 32 * 130 * 4
+    # splits of 8..32 tiles aiming at 1024 waves: 16 tiles x 2 KV heads -> 8-tile splits, 2 of them
+    assert need == 1 * 2 * 2 * 32 * 130 * 4
     cases = [(dict(struct_size=4), 3), (dict(D=256), 3), (dict(out_dtype=2), 3), (dict(Hkv=3), 3),
              (dict(S_q=9), 3),                   # 4 heads x 9 rows > 32 columns
              (dict(causal=2), 2), (dict(S_q=2, S_k=1), 3), (dict(tile_m=0), 2),

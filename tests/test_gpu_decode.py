@@ -67,8 +67,10 @@ def test_decode_parity(case):
 
 def test_decode_workspace_and_errors():
     m = L()
-    # splits of 2048 keys: 5000 keys are 3 splits
-    assert m.lamp_decode_workspace_bytes(2, 8, 5000, 128) == 2 * 8 * 3 * 32 * 130 * 4
+    # 79 tiles x 16 (b, KV head) groups -> 8-tile splits (the minimum), 10 of them
+    assert m.lamp_decode_workspace_bytes(2, 8, 5000, 128) == 2 * 8 * 10 * 32 * 130 * 4
+    # the Qwen3-8B-like step: 512 tiles x 64 groups -> 32-tile splits (the maximum)
+    assert m.lamp_decode_workspace_bytes(8, 8, 32768, 128) == 8 * 8 * 16 * 32 * 130 * 4
     x = torch.zeros((1, 40, 2, 128), dtype=torch.uint8, device=dev())
     s = torch.zeros((1, 40, 1), dtype=torch.float32, device=dev())
     kx = torch.zeros((1, 1, 64, 128), dtype=torch.uint8, device=dev())
