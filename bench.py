@@ -395,6 +395,44 @@ def other_workloads(torch, L):
     return out
 
 
+def component_times(torch, pipe, iters=20):
+    """Each enqueued part of a step timed alone with HIP events on the current
+    stream: the Q and K quantisers (HBM-bound; bytes read + written against
+    8 TB/s), the mask builder and the attention kernel."""
+    L, c = pipe.L, pipe.cfg
+    parts = {
+        "quantize_q": (lambda: L.lamp_quantize_blocks(pipe.qd, c.tile_m, c.code, codes=pipe.q8,
+                                                      scales=pipe.sq, seqlens=pipe.seqlens),
+                       3 * pipe.qd.numel() + 4 * pipe.sq.numel()),
+        "quantize_k": (lambda: L.lamp_quantize_blocks(pipe.kd, c.tile_n, c.code, codes=pipe.k8,
+                                                      scales=pipe.sk, seqlens=pipe.seqlens),
+                       3 * pipe.kd.numel() + 4 * pipe.sk.numel()),
+        "build_mask": (lambda: L.lamp_build_mask(c.B, c.Hq, c.S, c.S, c.tile_m, c.tile_n,
+                                                 c.tiles_per_bit, pipe.f16, c.mask_seed,
+                                                 c.words_per_row, mask=pipe.mask), None),
+        "attention": (pipe.attn, None),
+    }
+    out = {}
+    for name, (fn, nbytes) in parts.items():
+        fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(iters)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+        rec = {"ms": round(ms, 4)}
+        if nbytes is not None:
+            rec["bytes"] = int(nbytes)
+            rec["gbs"] = round(nbytes / ms / 1e6, 1)
+            rec["frac_hbm"] = round(nbytes / ms / 1e6 / (HBM_PEAK / 1e9), 4)
+        out[name] = rec
+    return out
+
+
 def time_attn(torch, pipe, iters, warmup):
     for _ in range(warmup):
         pipe.attn()
@@ -510,6 +548,8 @@ def main():
                      "peaks": {"int8_fp8": PEAK8, "bf16_fp16": PEAK16},
                      "kernel_source_sha256": kernel_source_hash()},
     }
+    result["components"] = component_times(torch, pipe)
+    log(f"[bench] components: {json.dumps(result['components'])}")
     sus = sustained_mfma_peaks(torch)
     if sus is not None:
         p8s, p16s = sus["int8_fp8"]["ops_per_s"], sus["bf16_fp16"]["ops_per_s"]
