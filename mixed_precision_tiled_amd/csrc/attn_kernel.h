@@ -120,6 +120,10 @@ void attn_fwd_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char sk1[SH::K16_BYTES];
   __shared__ __attribute__((aligned(1024))) char sv0[SH::V_BYTES];
   __shared__ __attribute__((aligned(1024))) char sv1[SH::V_BYTES];
+  // adaptive mode: an 8-bit tile is staged both as K8 (here) and as K16 (in
+  // sk0 / sk1), so that a flagged sub-block recomputes its logits from LDS
+  __shared__ __attribute__((aligned(1024))) char sq0[ADAPTIVE ? SH::K8_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char sq1[ADAPTIVE ? SH::K8_BYTES : 16];
 
   // ---- workgroup -> (b, h, qt): XCD-contiguous chunks of the logical order
   //      (kv-head group, b) major, query tile descending, head minor.  The
@@ -267,15 +271,19 @@ void attn_fwd_kernel(const AttnArgs a) {
     asm volatile("" : "+s"(v));
     return v;
   };
-  auto issue_k = [&](int kt, bool is8, char* kdst) {
+  // kdst: the K region (K16, or K8 outside the adaptive mode); kdst8: the
+  // adaptive mode's K8 buffer
+  auto issue_k = [&](int kt, bool is8, char* kdst, char* kdst8) {
     const int wu = wave_s();
     const uint32_t key0 = (uint32_t)(kt * SH::TN);
     if (is8) {
       const auto rs = make_rsrc(k8base + key0 * D, k8_bytes - key0 * D);
 #pragma unroll
       for (int j = 0; j < SH::JK8; ++j)
-        dma16_buf(rs, copy_off(off_k8, K8_1, j, (uint32_t)(RS8 * D)), 0u, kdst + 1024 * (wu + NW * j));
-    } else {
+        dma16_buf(rs, copy_off(off_k8, K8_1, j, (uint32_t)(RS8 * D)), 0u,
+                  (ADAPTIVE ? kdst8 : kdst) + 1024 * (wu + NW * j));
+    }
+    if (!is8 || ADAPTIVE) {
       const auto rs = make_rsrc(kbase + key0 * kss, k16_bytes - key0 * kss);
 #pragma unroll
       for (int j = 0; j < SH::JK16; ++j)
@@ -365,21 +373,6 @@ void attn_fwd_kernel(const AttnArgs a) {
       x[16 + i] = acc1[i];
     }
   };
-  auto qk16_global = [&](int key0, float* x) {
-#pragma unroll
-    for (int kb_ = 0; kb_ < 2; ++kb_) {
-      f32x16 acc = f32x16{};
-      const int key = min(key0 + kb_ * 32 + lr, key_max);
-      const char* kr = kbase + (uint32_t)key * kss;
-#pragma unroll
-      for (int t = 0; t < SH::NQ16; ++t) {
-        const u32x4 af = ld_global16(kr + 2 * (16 * t + 8 * hf));
-        acc = mfma16<BF16>(af, q16[t], acc);
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) x[kb_ * 16 + i] = acc[i];
-    }
-  };
   // int8 accumulator start value, kept in registers across the loop
   i32x16 acc_init;
 #pragma unroll
@@ -451,7 +444,9 @@ void attn_fwd_kernel(const AttnArgs a) {
     float c, xoff;
     bool is16, scaled;
   };
-  auto qk_part = [&](int kt, const char* kb, bool is8, float sK, float* x) -> Logits {
+  // kb: the K region (K16, or K8 outside the adaptive mode); kb8: the
+  // adaptive mode's K8 buffer
+  auto qk_part = [&](int kt, const char* kb, const char* kb8, bool is8, float sK, float* x) -> Logits {
     const int key0 = kt * SH::TN;
     const bool need_mask = rows_ragged || (key0 + SH::TN > Lk) ||
                            (a.causal && key0 + SH::TN - 1 > row0 + coff);
@@ -468,7 +463,7 @@ void attn_fwd_kernel(const AttnArgs a) {
       lg.scaled = true;
     };
     if (is8) {
-      qk8_lds(kb, key0, x);
+      qk8_lds(ADAPTIVE ? kb8 : kb, key0, x);
       lg.c = (sQ * sK) * sm * kLogScale;
       if constexpr (LAZY && !E4M3) lg.xoff = kMagic;
     } else {
@@ -490,9 +485,9 @@ void attn_fwd_kernel(const AttnArgs a) {
         if (wave_any(cond)) {
           lg.is16 = true;
           fword |= 1ull << (kt & 63);
-          // recompute the sub-block's logits at 16 bits, K16 straight from
-          // global memory (only flagged sub-blocks need it)
-          qk16_global(key0, x);
+          // recompute the sub-block's logits at 16 bits from the tile's K16
+          // copy in LDS
+          qk16_lds(kb, x);
           lg.c = sm;
           lg.scaled = false;
           if (need_mask) mask_scale();
@@ -699,25 +694,26 @@ void attn_fwd_kernel(const AttnArgs a) {
       pv_part(vb, pk);
     }
   };
-  issue_k(0, is8_cur, sk0);
+  issue_k(0, is8_cur, sk0, sq0);
   wait_vmem();
   __syncthreads();
   // FIRST: tile 0, which has no previous tile to multiply with V
-  auto step = [&](auto first, int kt, const char* kcur, char* knxt, const char* vprev, char* vcur) {
+  auto step = [&](auto first, int kt, const char* kcur, char* knxt, const char* kcur8, char* knxt8,
+                  const char* vprev, char* vcur) {
     constexpr bool FIRST = decltype(first)::value;
     bool is8_next = false;
     if (kt + 1 < kt_end) is8_next = next_tile_is8();
     // (after the mask bit, so that a wait for a reloaded mask word does not
     // also wait for this load)
     const float sk_n2 = kt + 2 < kt_end ? ld_uniform(sKp + kt + 2) : 0.f;
-    if (kt + 1 < kt_end) issue_k(kt + 1, is8_next, knxt);
+    if (kt + 1 < kt_end) issue_k(kt + 1, is8_next, knxt, knxt8);
     if constexpr (PV8) {
       if (is8_cur) svc_cur = (int)((__builtin_bit_cast(uint32_t, ld_uniform(sVp + kt)) >> 23) & 0xFFu);
     }
     issue_v(kt, is8_cur, vcur);
     if (kt < kt_end_w) {
       float x[32];
-      const Logits lg = qk_part(kt, kcur, is8_cur, sk_cur, x);
+      const Logits lg = qk_part(kt, kcur, kcur8, is8_cur, sk_cur, x);
       if constexpr (FIRST) {
         softmax_part(x, lg, pk, False_{});
       } else if constexpr (PV8) {
@@ -752,10 +748,10 @@ void attn_fwd_kernel(const AttnArgs a) {
     sk_cur = sk_n1;
     sk_n1 = sk_n2;
   };
-  if (kt_end > 0) step(True_{}, 0, sk0, sk1, sv1, sv0);
+  if (kt_end > 0) step(True_{}, 0, sk0, sk1, sq0, sq1, sv1, sv0);
   for (int kt = 1; kt < kt_end; kt += 2) {
-    step(False_{}, kt, sk1, sk0, sv0, sv1);
-    if (kt + 1 < kt_end) step(False_{}, kt + 1, sk0, sk1, sv1, sv0);
+    step(False_{}, kt, sk1, sk0, sq1, sq0, sv0, sv1);
+    if (kt + 1 < kt_end) step(False_{}, kt + 1, sk0, sk1, sq0, sq1, sv1, sv0);
   }
   // P V of the last tile (its V was copied in the last step)
   if (kt_end_w == kt_end && kt_end > 0) {
