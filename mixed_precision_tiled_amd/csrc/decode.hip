@@ -205,8 +205,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   }
 
   // partial of this split: O^T block db holds rows d = 32 db + 8 (r / 4) +
-  // 4 hf + r % 4 of column lr
+  // 4 hf + r % 4 of column lr.  Only live columns are written (the merge
+  // reads no others).
   const float l_tot = halves_sum(l_run);
+  if (!col_live) return;
   const int64_t slot = ((int64_t)grp * a.n_split + split) * 32 + lr;
   float* wo = a.ws_o + slot * D;
 #pragma unroll
