@@ -36,20 +36,26 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantArgs a) {
                      2 * (b * a.sb + h * a.sh + (int64_t)r0 * a.ss);
   const int tid = threadIdx.x;
 
+  // every load is issued unconditionally (a dead chunk reads chunk 0 of the
+  // block, which exists, and is zeroed afterwards), so that a thread's loads
+  // are in flight together instead of one at a time
   u32x4 cache[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = tid + i * kQuantThreads;
+    const int cl = (c < nch && c / cpr < rows_live) ? c : 0;
+    const int r = cl / cpr, col = (cl % cpr) * 8;
+    cache[i] = ld_global16(base + 2 * ((int64_t)r * a.ss + col));
+  }
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const int c = tid + i * kQuantThreads;
-    cache[i] = u32x4{0u, 0u, 0u, 0u};
-    if (c < nch && c / cpr < rows_live) {
-      const int r = c / cpr, col = (c % cpr) * 8;
-      cache[i] = ld_global16(base + 2 * ((int64_t)r * a.ss + col));
+    if (!(c < nch && c / cpr < rows_live)) cache[i] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        amax = fmaxf(amax, fabsf(from16<BF16>(cache[i][e] & 0xFFFFu)));
-        amax = fmaxf(amax, fabsf(from16<BF16>(cache[i][e] >> 16)));
-      }
+    for (int e = 0; e < 4; ++e) {
+      amax = fmaxf(amax, fabsf(from16<BF16>(cache[i][e] & 0xFFFFu)));
+      amax = fmaxf(amax, fabsf(from16<BF16>(cache[i][e] >> 16)));
     }
   }
   // block absmax: wave butterfly, then across the 4 waves through LDS
@@ -134,8 +140,10 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_v_kernel(VQuantArgs a)
   const char* base = reinterpret_cast<const char*>(a.v) + 2 * (b * a.sb + h * a.sh);
   const int tid = threadIdx.x;
 
-  float val[HRT][32];
-  float amax = 0.f;
+  // every load is issued unconditionally from a clamped key (row S - 1
+  // exists) and dead elements are zeroed afterwards, so that a thread's
+  // loads are in flight together instead of one at a time
+  uint16_t raw[HRT][32];
 #pragma unroll
   for (int i = 0; i < HRT; ++i) {
     const int hr = tid + i * kQuantThreads;
@@ -143,9 +151,19 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_v_kernel(VQuantArgs a)
 #pragma unroll
     for (int p = 0; p < 32; ++p) {
       const int key = kt * 64 + 32 * (p >> 4) + 8 * ((p & 15) >> 2) + (p & 3) + 4 * c;
-      float x = 0.f;
-      if (hr < 2 * D && key < len)
-        x = from16<BF16>(*reinterpret_cast<const uint16_t*>(base + 2 * ((int64_t)key * a.ss + d)));
+      raw[i][p] = *reinterpret_cast<const uint16_t*>(base + 2 * ((int64_t)min(key, a.S - 1) * a.ss + d));
+    }
+  }
+  float val[HRT][32];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < HRT; ++i) {
+    const int hr = tid + i * kQuantThreads;
+    const int c = hr / D;
+#pragma unroll
+    for (int p = 0; p < 32; ++p) {
+      const int key = kt * 64 + 32 * (p >> 4) + 8 * ((p & 15) >> 2) + (p & 3) + 4 * c;
+      const float x = (hr < 2 * D && key < len) ? from16<BF16>(raw[i][p]) : 0.f;
       val[i][p] = x;
       amax = fmaxf(amax, fabsf(x));
     }
