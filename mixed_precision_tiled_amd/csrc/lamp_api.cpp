@@ -181,7 +181,8 @@ lamp_status build_mask_common(int64_t B, int64_t Hq, int64_t S_q, int64_t S_k, i
   lamp::MaskArgs a{};
   a.mask = mask;
   a.total_words = B * Hq * n_qt * words_per_row;
-  if (cdiv(a.total_words, 256) > kMaxGrid) return fail(LAMP_ERR_UNSUPPORTED, "mask too large");
+  if (cdiv(a.total_words, lamp::kMaskWordsPerBlock) > kMaxGrid)
+    return fail(LAMP_ERR_UNSUPPORTED, "mask too large");
   a.seed = seed;
   a.threshold = frac_per_head ? 0 : frac_threshold(frac_16bit);
   a.words_per_row = words_per_row;

@@ -30,6 +30,7 @@ struct VQuantArgs {
 };
 
 constexpr int kMaskMaxHeads = 128;      // per-head fractions ride in the kernel arguments
+constexpr int kMaskWordsPerBlock = 4;    // random-mask builder: one wave per word
 
 struct MaskArgs {
   uint64_t* mask;

@@ -226,22 +226,23 @@ __device__ __forceinline__ uint64_t splitmix64(uint64_t seed, uint64_t n) {
   return z ^ (z >> 31);
 }
 
-__global__ __launch_bounds__(256) void build_mask_kernel(MaskArgs a) {
-  const int64_t wid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (wid >= a.total_words) return;
+// One wave per mask word: lane i hashes group 64 w + i and the wave's ballot
+// is the word (groups past n_g give 0 bits).
+__global__ __launch_bounds__(64 * kMaskWordsPerBlock) void build_mask_kernel(MaskArgs a) {
+  const int64_t wid = (int64_t)blockIdx.x * kMaskWordsPerBlock + (threadIdx.x >> 6);
+  if (wid >= a.total_words) return;                 // uniform across the wave
+  const int lane = (int)(threadIdx.x & 63u);
   const int64_t row = wid / a.words_per_row;        // (b*Hq + h)*n_qt + qt
   const int w = (int)(wid % a.words_per_row);
   const uint64_t thr = a.per_head ? a.head_threshold[(row / a.n_qt) % a.Hq] : a.threshold;
-  uint64_t word = 0;
-  const int g0 = w * 64;
-  const int gn = min(64, a.n_g - g0);
-  for (int i = 0; i < gn; ++i) {
-    const uint64_t idx = (uint64_t)row * (uint64_t)a.n_g + (uint64_t)(g0 + i);
-    const uint64_t r = splitmix64(a.seed, idx);
-    const bool is16 = (r >> 32) < thr;
-    word |= (uint64_t)(!is16) << i;
+  const int g = w * 64 + lane;
+  bool is8 = false;
+  if (g < a.n_g) {
+    const uint64_t idx = (uint64_t)row * (uint64_t)a.n_g + (uint64_t)g;
+    is8 = !((splitmix64(a.seed, idx) >> 32) < thr);
   }
-  a.mask[wid] = word;
+  const uint64_t word = (uint64_t)__ballot(is8);
+  if (lane == 0) a.mask[wid] = word;
 }
 
 // Structured template: one thread per mask word; the rule depends only on
@@ -285,8 +286,8 @@ hipError_t launch_quantize_v(const VQuantArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_build_mask(const MaskArgs& a, hipStream_t s) {
-  const unsigned blocks = (unsigned)((a.total_words + 255) / 256);
-  hipLaunchKernelGGL(build_mask_kernel, dim3(blocks), dim3(256), 0, s, a);
+  const unsigned blocks = (unsigned)((a.total_words + kMaskWordsPerBlock - 1) / kMaskWordsPerBlock);
+  hipLaunchKernelGGL(build_mask_kernel, dim3(blocks), dim3(64 * kMaskWordsPerBlock), 0, s, a);
   return hipGetLastError();
 }
 
