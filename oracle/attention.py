@@ -218,12 +218,51 @@ def attn_tilemix(P, b, h, rows):
     return O, lse
 
 
+def _err_logits_tilemix(P, b, h, rows, cols, s, r8, m_row):
+    """Bound on the error of an fp32 evaluation of the max-shifted exponent
+    s - m under mask routing (natural-log units), for any reference m the
+    evaluation chooses: exact 8-bit integer products (int8) or exact products
+    summed in fp32 in any order (e4m3, 16-bit: gamma_D * sum|products| *
+    scale, Higham eq. (3.5)), a scale product of a few fp32 roundings that
+    may be cut to 21 significant bits, and one rounding of the shifted
+    exponent: 20u(|s| + |m|) covers the latter two with room."""
+    D = P.D
+    gam = D * U32 / (1 - D * U32)
+    sm = P.sm_scale
+    e = gam * sm * (np.abs(P.q[b, h][rows]) @ np.abs(P.k[b, P.kvh(h)][cols]).T)
+    if P.code == "i8":
+        e8 = np.zeros_like(s)
+    else:
+        sq = P.q_scales[b, h].astype(np.float64)[rows // P.tile_m]
+        sk = P.k_scales[b, P.kvh(h)].astype(np.float64)[cols // P.tile_n]
+        e8 = gam * (np.abs(P.qv[b, h][rows]) @ np.abs(P.kv[b, P.kvh(h)][cols]).T) \
+            * sq[:, None] * sk[None, :] * sm
+    return np.where(r8, e8, e) + 20 * U32 * (np.abs(s) + np.abs(m_row)[:, None])
+
+
+def tilemix_bounds(P, b, h, rows, dtype="bf16"):
+    """``attn_tilemix`` with a bound on the LSE error of an fp32 evaluation
+    whose exponents carry errors within ``_err_logits_tilemix``: at most
+    max_j E_j, plus half an ulp of the 16-bit weights that the normaliser
+    sums, fp16 subnormal weights (2^-25 each against l >= 1) and fp32
+    rounding of the sum and the logarithm.  Returns (O [R, D], LSE [R],
+    lse_tol [R])."""
+    rows = np.asarray(rows)
+    s, r8, ok = routed_logits(P, b, h, rows)
+    none = ~ok.any(axis=1)
+    m = np.where(none, 0.0, np.where(ok, s, -np.inf).max(axis=1))
+    sf = np.where(ok, s, 0.0)
+    E = np.where(ok, _err_logits_tilemix(P, b, h, rows, np.arange(P.S_k), sf, r8, m), 0.0)
+    O, lse = attn_tilemix(P, b, h, rows)
+    sub16 = 0.0 if dtype == "bf16" else ok.sum(axis=1) * 2.0 ** -25
+    lse_tol = (E.max(axis=1, initial=0.0) + np.log1p(_sum16_rel(dtype)) + sub16
+               + (P.n_kt + 64) * U32 + 4 * U32 * np.abs(np.where(none, 0.0, lse)))
+    return O, lse, lse_tol
+
+
 # ---------------------------------------------------------------------------
 # LampAttention: tile-by-tile emulation
 # ---------------------------------------------------------------------------
-
-_P8_CACHE = {}
-
 
 def exp8_of_code(codes):
     """p = E4M3(exp(val(code))) for e4m3 codes of non-positive logits."""
@@ -236,22 +275,46 @@ def exp8(x):
 
 
 @dataclass
+class LampBranch:
+    """One sequence of outcomes of a sub-block's adaptive flag decisions.
+
+    A decision whose margin lies within the bound on the GPU's fp32 error is
+    evaluated both ways; each leaf of that tree is one branch, identified by
+    its flags (two branches differ in the flag of the tile where they split).
+    """
+    flags: np.ndarray             # [n_kt] bool: sub-block recomputed in 16-bit at key tile kt
+    dontcare: np.ndarray          # [n_kt] bool: decision at kt within the error bound (split)
+    margin: np.ndarray            # [n_kt] max(s8 - m') + tau of the decision (nan: none)
+    bound: np.ndarray             # [n_kt] error bound of that margin
+    O: np.ndarray                 # [r, D]
+    lse: np.ndarray               # [r]
+    extra_tol: np.ndarray         # [r, D] widening for possible e4m3 rounding flips
+    lse_tol: np.ndarray           # [r] bound on |LSE_gpu - LSE|
+    counts: dict = field(default_factory=dict)
+
+
+@dataclass
 class LampResult:
-    O: np.ndarray
-    lse: np.ndarray
-    flags: np.ndarray             # [n_sb_rows, n_kt] bool, sub-block recomputed in 16-bit
-    flag_dontcare: np.ndarray     # [n_sb_rows, n_kt] bool, decision within the GPU error bound
-    fragile_rows: np.ndarray      # [R] bool, rows excluded from pass/fail
-    extra_tol: np.ndarray         # [R] widening of the per-row tolerance (exp8 flips)
+    O: np.ndarray                 # [R, D] of the primary branch (the oracle's own decisions)
+    lse: np.ndarray               # [R]
+    flags: np.ndarray             # [n_sb, n_kt] bool, primary branch
+    flag_dontcare: np.ndarray     # [n_sb, n_kt] bool, primary branch's decisions within the bound
+    extra_tol: np.ndarray         # [R, D]
+    lse_tol: np.ndarray           # [R]
+    branches: list                # per sub-block (sorted order): [LampBranch], [0] = primary
+    row_branch: list              # per sub-block: indices (into the R rows) of its rows
+    unresolved: np.ndarray        # [n_sb] bool: more branches than the cap (the rest dropped)
     counts: dict = field(default_factory=dict)
 
 
 def _err_logits(P, b, h, rows, cols, s, use16):
-    """Bound on the GPU's fp32 error in each logit (see design notes).
+    """Bound on the GPU's fp32 error in each logit s (natural-log units).
 
     8-bit int8: the accumulator is exact; the scale product and the final
     multiply add at most 3 roundings -> 4u|s|.  8-bit e4m3 and 16-bit: exact
-    products summed in fp32 -> gamma_D * sum|products| * scale, plus 4u|s|.
+    products summed in fp32 in any order -> gamma_D * sum|products| * scale
+    (Higham, "Accuracy and Stability of Numerical Algorithms", 2nd ed.,
+    eq. (3.5)), plus 4u|s| for the scale roundings and the product.
     """
     D = P.D
     gam = D * U32 / (1 - D * U32)
@@ -268,33 +331,47 @@ def _err_logits(P, b, h, rows, cols, s, use16):
     return np.where(use16, e16, e8) + 4 * U32 * np.abs(s)
 
 
-def attn_lamp(P, b, h, sub_blocks):
-    """Emulate the online softmax for the given sub-blocks (indices of
-    sub_rows-row blocks of head (b, h)); rows processed together, key tiles in
-    ascending order."""
-    sr = P.sub_rows
-    sub_blocks = np.asarray(sub_blocks, dtype=np.int64)
-    rows = (sub_blocks[:, None] * sr + np.arange(sr)[None, :]).reshape(-1)
-    rows = rows[rows < P.S_q]
-    sbid = rows // sr                                   # sub-block of each row
-    usb, sb_idx = np.unique(sbid, return_inverse=True)  # local sub-block index per row
+def _sum16_rel(dtype):
+    """Relative rounding of one weight to the 16-bit P operand (half an ulp)."""
+    return 2.0 ** -8 if dtype == "bf16" else 2.0 ** -11
+
+
+class _State:
+    """Online-softmax state of a group of rows along one branch."""
+
+    def __init__(self, R, D, n_kt):
+        self.m = np.full(R, -np.inf)
+        self.em = np.zeros(R)             # bound on |m_gpu - m_ref|
+        self.l = np.zeros(R)
+        self.acc = np.zeros((R, D))
+        self.fp = np.zeros(R)             # sum of possible weight flips (alpha-scaled)
+        self.fpv = np.zeros((R, D))       # the same times |v| per head dim
+        self.xerr = np.zeros(R)           # largest exponent error bound of an fp32 weight
+        self.nvalid_row = np.zeros(R)
+        self.flags = np.zeros(n_kt, dtype=bool)
+        self.dontcare = np.zeros(n_kt, dtype=bool)
+        self.margin = np.full(n_kt, np.nan)
+        self.bound = np.full(n_kt, np.nan)
+        self.counts = dict(n8=0, n16=0, nflag=0, nvalid=0)
+
+    def copy(self):
+        c = _State.__new__(_State)
+        for k, v in self.__dict__.items():
+            c.__dict__[k] = dict(v) if isinstance(v, dict) else v.copy()
+        return c
+
+
+def _lamp_group(P, b, h, rows, perturb, max_branches, dtype):
+    """Branches of one group of rows (one sub-block in the adaptive mode,
+    every requested row otherwise)."""
     R, D = len(rows), P.D
     vh = P.v[b, P.kvh(h)]
+    vabs = np.abs(vh)
+    vabs8 = np.abs(P.v8[b, P.kvh(h)]) if P.pv8 else vabs
     r8_tiles = P.route8_tiles(b, h)
     qt = rows // P.tile_m
-
-    m = np.full(R, -np.inf)
-    em = np.zeros(R)                      # bound on |m_gpu - m_ref|
-    l = np.zeros(R)
-    acc = np.zeros((R, D))
-    flags = np.zeros((len(usb), P.n_kt), dtype=bool)
-    dontcare = np.zeros((len(usb), P.n_kt), dtype=bool)
-    diverged = np.zeros(len(usb), dtype=bool)
-    frag_p = np.zeros(R)                  # sum of possible p flips
-    frag_pv = np.zeros(R)                 # sum of p flips times max|v_j|
-    vmax = np.abs(vh).max(axis=1)
-    n8 = n16 = nflag = nvalid = 0
-
+    states = [_State(R, D, P.n_kt)]
+    unresolved = False
     for kt in range(P.n_kt):
         cols = np.arange(kt * P.tile_n, min(P.S_k, (kt + 1) * P.tile_n))
         ok = P.valid(rows, cols, b)
@@ -303,78 +380,168 @@ def attn_lamp(P, b, h, sub_blocks):
         r8 = r8_tiles[qt, kt][:, None] & ok             # valid and 8-bit routed
         s8 = logits8(P, b, h, rows, cols)
         s16 = logits16(P, b, h, rows, cols)
-        flag_row = np.zeros(R, dtype=bool)
-        if P.adaptive:
-            s8v = np.where(r8, s8, -np.inf)
-            rowmax8 = s8v.max(axis=1)
-            e8 = _err_logits(P, b, h, rows, cols, s8, np.zeros_like(ok))
-            has8 = r8.any(axis=1)
-            mprime = np.maximum(m, rowmax8)
-            with np.errstate(invalid="ignore"):
-                d_row = np.where(has8, rowmax8 - mprime, -np.inf)
-            e_row = np.where(has8, np.where(r8, e8, 0).max(axis=1, initial=0) + em, 0.0)
-            for i_sb in range(len(usb)):
-                sel = (sb_idx == i_sb) & has8
-                if not sel.any():
-                    continue
-                dmax = d_row[sel].max() + P.tau
-                flagged = dmax >= 0
-                flags[i_sb, kt] = flagged
-                if abs(dmax) <= 2 * e_row[sel].max() + 4 * U32 * (abs(P.tau) + 1):
-                    dontcare[i_sb, kt] = True
-                    diverged[i_sb] = True
-                if diverged[i_sb]:
-                    dontcare[i_sb, kt] = True
-                if flagged:
-                    flag_row |= (sb_idx == i_sb)
-        use16 = (~r8_tiles[qt, kt])[:, None] | flag_row[:, None]
-        use16 = np.broadcast_to(use16, ok.shape)
-        s = np.where(use16, s16, s8)
-        sv = np.where(ok, s, -np.inf)
-        m_new = np.maximum(m, sv.max(axis=1))
-        es = _err_logits(P, b, h, rows, cols, s, use16)
-        em = np.where(np.isfinite(m_new), np.maximum(em, np.where(ok, es, 0).max(axis=1)), em)
-        with np.errstate(invalid="ignore"):
-            x = np.where(ok, s - m_new[:, None], -np.inf)
-        p16 = np.exp(x)
-        if P.exp8:
-            xc = np.maximum(np.where(ok, x, -448.0), -448.0)
-            p8 = exp8(xc)
-            ex = es + em[:, None] + 2 * U32 * (np.abs(xc) + np.abs(s))
-            lo = exp8(np.maximum(xc - ex, -448.0))
-            hi = exp8(np.minimum(xc + ex, 0.0))
-            dp = np.where(ok & ~use16, hi - lo, 0.0)
-            frag_p += dp.sum(axis=1)
-            frag_pv += (dp * vmax[cols][None, :]).sum(axis=1)
-        else:
-            p8 = p16
-        p = np.where(ok, np.where(use16, p16, p8), 0.0)
-        with np.errstate(invalid="ignore"):
-            alpha = np.where(np.isfinite(m), np.exp(m - m_new), 0.0)
-        alpha = np.where(np.isfinite(m_new), alpha, 1.0)
-        l = alpha * l + p.sum(axis=1)
-        if P.pv8:
-            # 8-bit weights meet the e4m3 V codes of their tile (products exact)
-            p8v = np.where(use16, 0.0, p)
-            acc = alpha[:, None] * acc + (p - p8v) @ vh[cols] + p8v @ P.v8[b, P.kvh(h)][cols]
-        else:
-            acc = alpha[:, None] * acc + p @ vh[cols]
-        m = np.where(np.isfinite(m_new), m_new, m)
-        n8 += int((ok & r8).sum())
-        n16 += int((ok & ~np.broadcast_to(r8_tiles[qt, kt][:, None], ok.shape)).sum())
-        nflag += int((ok & r8 & flag_row[:, None]).sum())
-        nvalid += int(ok.sum())
+        e8 = _err_logits(P, b, h, rows, cols, s8, np.zeros(ok.shape, dtype=bool))
+        e16 = _err_logits(P, b, h, rows, cols, s16, np.ones(ok.shape, dtype=bool))
+        if perturb is not None:
+            s8 = s8 + perturb(e8)
+            s16 = s16 + perturb(e16)
+        has8 = r8.any(axis=1)
+        nxt = []
+        for st in states:
+            outcomes, split = [False], False
+            if P.adaptive and has8.any():
+                rowmax8 = np.where(r8, s8, -np.inf).max(axis=1)
+                mprime = np.maximum(st.m, rowmax8)
+                with np.errstate(invalid="ignore"):
+                    d_row = rowmax8 - mprime
+                e_row = np.where(r8, e8, 0).max(axis=1) + st.em
+                dmax = d_row[has8].max() + P.tau
+                bnd = 2 * e_row[has8].max() + 4 * U32 * (abs(P.tau) + 1)
+                flagged = bool(dmax >= 0)
+                outcomes = [flagged]
+                st.margin[kt], st.bound[kt] = dmax, bnd
+                if abs(dmax) <= bnd:
+                    outcomes, split = [flagged, not flagged], True
+            for i, fl in enumerate(outcomes):
+                c = st if i == len(outcomes) - 1 else st.copy()
+                c.dontcare[kt] = split
+                _lamp_tile(P, c, kt, cols, ok, r8, r8_tiles[qt, kt], s8, s16, e8, e16, fl,
+                           vh, vabs8, b, h)
+                nxt.append(c)
+        if len(nxt) > max_branches:
+            unresolved = True
+            nxt = nxt[:max_branches]
+        states = nxt
 
-    none = l == 0                        # rows with no valid key: O = 0, LSE = -inf
-    l_safe = np.where(none, 1.0, l)
-    O = acc / l_safe[:, None]
-    with np.errstate(divide="ignore"):
-        lse = np.where(none, -np.inf, m + np.log(l_safe))
-    fragile_rows = diverged[sb_idx]
-    extra = (frag_pv + frag_p * np.abs(O).max(axis=1)) / l_safe
-    counts = dict(n8=n8, n16=n16, nflag=nflag, nvalid=nvalid)
-    return LampResult(O=O, lse=lse, flags=flags, flag_dontcare=dontcare,
-                      fragile_rows=fragile_rows, extra_tol=extra, counts=counts), rows, usb
+    u16 = _sum16_rel(dtype)
+    branches = []
+    for st in states:
+        none = st.l == 0                 # rows with no valid key: O = 0, LSE = -inf
+        l_safe = np.where(none, 1.0, st.l)
+        O = st.acc / l_safe[:, None]
+        with np.errstate(divide="ignore"):
+            lse = np.where(none, -np.inf, st.m + np.log(l_safe))
+        denom = np.maximum(l_safe - st.fp, 1e-300)
+        extra = (st.fpv + st.fp[:, None] * np.abs(O)) / denom[:, None]
+        sub16 = 0.0 if dtype == "bf16" else st.nvalid_row * 2.0 ** -25
+        # LSE = m + ln l: the GPU's m is off by at most em, an fp32 weight
+        # by its exponent's error (xerr), the e4m3 weights by the flips
+        # summed in fp (relative to l - fp); plus the 16-bit rounding of fp32
+        # weights (exp8 weights are exact in 16 bits), fp16 subnormal
+        # weights, and fp32 rounding of the sum and the log
+        lse_tol = (st.em + st.xerr + np.log1p(st.fp / denom) + np.log1p(u16) + sub16
+                   + 4 * U32 * np.abs(np.where(none, 0.0, lse)) + (P.n_kt + 64) * U32)
+        branches.append(LampBranch(flags=st.flags, dontcare=st.dontcare, margin=st.margin,
+                                   bound=st.bound, O=O, lse=lse,
+                                   extra_tol=extra, lse_tol=lse_tol, counts=st.counts))
+    return branches, unresolved
+
+
+def _lamp_tile(P, st, kt, cols, ok, r8, tile_is8, s8, s16, e8, e16, flag, vh, vabs8, b, h):
+    """Update one branch's state with key tile kt (flag: its sub-block is
+    recomputed in 16-bit)."""
+    use16 = np.broadcast_to((~tile_is8)[:, None] | flag, ok.shape)
+    s = np.where(use16, s16, s8)
+    es = np.where(use16, e16, e8)
+    sv = np.where(ok, s, -np.inf)
+    m_new = np.maximum(st.m, sv.max(axis=1))
+    fin = np.isfinite(m_new)
+    st.em = np.where(fin, np.maximum(st.em, np.where(ok, es, 0).max(axis=1)), st.em)
+    with np.errstate(invalid="ignore"):
+        x = np.where(ok, s - m_new[:, None], -np.inf)
+    p16 = np.exp(x)
+    if P.exp8:
+        xc = np.maximum(np.where(ok, x, -448.0), -448.0)
+        p8 = exp8(xc)
+        ex = es + st.em[:, None] + 2 * U32 * (np.abs(xc) + np.abs(s))
+        lo = exp8(np.maximum(xc - ex, -448.0))
+        hi = exp8(np.minimum(xc + ex, 0.0))
+        dp = np.where(ok & ~use16, hi - lo, 0.0)
+        fp32w = ok & use16
+    else:
+        p8 = p16
+        dp = np.zeros(ok.shape)
+        fp32w = ok
+    e32 = es + 2 * U32 * (np.abs(np.where(ok, x, 0)) + np.abs(s))
+    st.xerr = np.maximum(st.xerr, np.where(fp32w, e32, 0).max(axis=1))
+    p = np.where(ok, np.where(use16, p16, p8), 0.0)
+    with np.errstate(invalid="ignore"):
+        alpha = np.where(np.isfinite(st.m), np.exp(st.m - m_new), 0.0)
+    alpha = np.where(fin, alpha, 1.0)
+    st.l = alpha * st.l + p.sum(axis=1)
+    st.fp = alpha * st.fp + dp.sum(axis=1)
+    st.fpv = alpha[:, None] * st.fpv + dp @ vabs8[cols]
+    if P.pv8:
+        # 8-bit weights meet the e4m3 V codes of their tile (products exact)
+        p8v = np.where(use16, 0.0, p)
+        st.acc = alpha[:, None] * st.acc + (p - p8v) @ vh[cols] + p8v @ P.v8[b, P.kvh(h)][cols]
+    else:
+        st.acc = alpha[:, None] * st.acc + p @ vh[cols]
+    st.m = np.where(fin, m_new, st.m)
+    st.nvalid_row += ok.sum(axis=1)
+    st.flags[kt] = flag
+    st.counts["n8"] += int(r8.sum())
+    st.counts["n16"] += int((ok & ~np.broadcast_to(tile_is8[:, None], ok.shape)).sum())
+    st.counts["nflag"] += int(r8.sum()) if flag else 0
+    st.counts["nvalid"] += int(ok.sum())
+
+
+def attn_lamp(P, b, h, sub_blocks, *, perturb=None, max_branches=64, dtype="bf16"):
+    """Emulate the online softmax for the given sub-blocks (indices of
+    sub_rows-row blocks of head (b, h)), key tiles in ascending order.
+
+    In the adaptive mode every sub-block is emulated on its own, and a flag
+    decision within the GPU error bound of the threshold is taken both ways
+    (at most ``max_branches`` branches per sub-block).  ``perturb`` (tests
+    only) maps the error bound of each logit to an offset added to it, to
+    emulate a GPU within the bound.  ``dtype`` is the 16-bit type of the
+    weights fed to P V (for the LSE bound).
+
+    Returns (LampResult, rows, sorted sub-block indices)."""
+    sr = P.sub_rows
+    sub_blocks = np.asarray(sub_blocks, dtype=np.int64)
+    rows = (sub_blocks[:, None] * sr + np.arange(sr)[None, :]).reshape(-1)
+    rows = rows[rows < P.S_q]
+    rows = np.unique(rows)
+    sbid = rows // sr
+    usb, sb_idx = np.unique(sbid, return_inverse=True)
+    R, D = len(rows), P.D
+    if P.adaptive:
+        groups = [np.flatnonzero(sb_idx == i) for i in range(len(usb))]
+    else:
+        groups = [np.arange(R)]
+    O = np.zeros((R, D))
+    lse = np.zeros(R)
+    extra = np.zeros((R, D))
+    lse_tol = np.zeros(R)
+    flags = np.zeros((len(usb), P.n_kt), dtype=bool)
+    dontcare = np.zeros((len(usb), P.n_kt), dtype=bool)
+    branches, row_branch = [], []
+    unresolved = np.zeros(len(usb), dtype=bool)
+    counts = dict(n8=0, n16=0, nflag=0, nvalid=0)
+    for gi, idx in enumerate(groups):
+        brs, unres = _lamp_group(P, b, h, rows[idx], perturb, max_branches, dtype)
+        pr = brs[0]
+        O[idx], lse[idx], extra[idx], lse_tol[idx] = pr.O, pr.lse, pr.extra_tol, pr.lse_tol
+        for k in counts:
+            counts[k] += pr.counts[k]
+        if P.adaptive:
+            flags[gi], dontcare[gi] = pr.flags, pr.dontcare
+            branches.append(brs)
+            row_branch.append(idx)
+            unresolved[gi] = unres
+        else:
+            # one branch for all rows: split it per sub-block
+            for i in range(len(usb)):
+                sel = np.flatnonzero(sb_idx[idx] == i)
+                branches.append([LampBranch(flags=pr.flags, dontcare=pr.dontcare, margin=pr.margin,
+                                            bound=pr.bound, O=pr.O[sel],
+                                            lse=pr.lse[sel], extra_tol=pr.extra_tol[sel],
+                                            lse_tol=pr.lse_tol[sel], counts={})])
+                row_branch.append(idx[sel])
+    return LampResult(O=O, lse=lse, flags=flags, flag_dontcare=dontcare, extra_tol=extra,
+                      lse_tol=lse_tol, branches=branches, row_branch=row_branch,
+                      unresolved=unresolved, counts=counts), rows, usb
 
 
 def uses_lamp(P):

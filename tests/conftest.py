@@ -25,3 +25,22 @@ def pytest_collection_modifyitems(config, items):
     for it in items:
         if "gpu" in it.keywords:
             it.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """One line with the LampAttention acceptance counts of the GPU parity
+    tests (flag decisions within the error bound evaluated both ways, flag
+    mismatches, rows excluded, widening for e4m3 rounding flips)."""
+    try:
+        from gpu_util import LAMP_REPORT
+    except Exception:  # pragma: no cover
+        return
+    if LAMP_REPORT:
+        r = LAMP_REPORT
+        terminalreporter.write_line(
+            "lamp acceptance: sub-blocks {} | decisions within the error bound (both ways) {} | "
+            "non-primary branches picked {} | flag mismatches {} | branch-cap overflows {} | "
+            "rows excluded {} | max e4m3-flip widening {:.2e} | max |O - oracle| {:.2e}".format(
+                r.get("n_subblocks", 0), r.get("n_split", 0), r.get("n_nonprimary", 0),
+                r.get("flag_mismatch", 0), r.get("unresolved", 0), r.get("excluded_rows", 0),
+                r.get("max_extra", 0.0), r.get("max_err", 0.0)))

@@ -3,6 +3,21 @@ binding and build the oracle's view of the same seeded inputs."""
 import numpy as np
 import torch
 
+# LampAttention acceptance counts over the session (printed at the end of the
+# run by conftest.py): sub-blocks checked, flag decisions within the error
+# bound (evaluated both ways), sub-blocks whose GPU flags picked a non-primary
+# branch, flag mismatches, branch-cap overflows, rows excluded (always 0) and
+# the largest widening for e4m3 rounding flips.
+LAMP_REPORT = {}
+
+
+def record_lamp(st):
+    for k in ("n_subblocks", "n_split", "n_branches", "n_nonprimary", "flag_mismatch",
+              "unresolved", "excluded_rows", "lse_bad", "n_bad"):
+        LAMP_REPORT[k] = LAMP_REPORT.get(k, 0) + int(st.get(k, 0))
+    LAMP_REPORT["max_extra"] = max(LAMP_REPORT.get("max_extra", 0.0), float(st.get("max_extra", 0.0)))
+    LAMP_REPORT["max_err"] = max(LAMP_REPORT.get("max_err", 0.0), float(st.get("max_err", 0.0)))
+
 from oracle import attention as A
 from oracle import mask as omask
 

@@ -1,0 +1,286 @@
+"""Pins of the oracle's error model: the bounds that decide where the GPU may
+differ from the oracle (flag decisions near the LampAttention threshold,
+e4m3 rounding flips, fp32 exponent errors) must (1) hold for fp32
+evaluations in any summation order, (2) be small enough to check something,
+and (3) accept every result that an fp32 evaluation within the bounds can
+produce, with flags differing only at decisions the oracle evaluates both
+ways.
+
+Sources: "LampAttention: Look-Ahead Mixed-Precision FlashAttention for
+Dedicated Accelerators", Abstract (8-bit products and exponentials, sensitive
+sub-blocks recomputed in 16 bits); "TileMix: Mixed-Precision Attention for
+Faster LLM Prefill", section 2 "The Dual-Path Engine" (per-block scales, one
+shared online softmax).  The bound on a sum of n products in fp32 is Higham,
+"Accuracy and Stability of Numerical Algorithms", 2nd ed., eq. (3.5).
+"""
+import numpy as np
+import pytest
+
+from oracle import attention as A
+from oracle import compare
+from synthetic import Config, make_inputs
+
+U = 2.0 ** -24
+
+
+def problem(D=128, S=512, code="e4m3", outliers=True, adaptive=True, exp8=True, tau=4.0,
+            f16=0.0, dtype="bf16", seed=5, Hq=2, Hkv=1, scale=1.0):
+    cfg = Config("pin", B=1, Hq=Hq, Hkv=Hkv, S=S, D=D, causal=True, dtype=dtype, tile_m=128,
+                 tile_n=64, tiles_per_bit=1, frac_16bit=f16, code=code, exp8=exp8,
+                 adaptive=adaptive, tau=tau, outliers=outliers, input_seed=seed,
+                 mask_seed=seed + 1, input_scale=scale)
+    q, k, v = make_inputs(cfg)
+    return A.make_problem(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                          causal=True, code=code, tile_m=128, tile_n=64, tiles_per_bit=1,
+                          frac_16bit=f16, seed=cfg.mask_seed, adaptive=adaptive, exp8=exp8,
+                          tau=tau, sub_rows=32)
+
+
+# ---------------------------------------------------------------------------
+# (1) the logit bound holds for fp32 sums in several orders
+# ---------------------------------------------------------------------------
+
+def f32(x):
+    return np.asarray(x, dtype=np.float32)
+
+
+def sum_orders(prod):
+    """fp32 sums over the last axis of exactly representable fp32 products,
+    in five orders: ascending, descending, pairwise, 16 interleaved partial
+    sums (one per k mod 16) added at the end, and numpy's own."""
+    n = prod.shape[-1]
+    out = []
+    acc = np.zeros(prod.shape[:-1], dtype=np.float32)
+    for i in range(n):
+        acc = f32(acc + prod[..., i])
+    out.append(acc)
+    acc = np.zeros(prod.shape[:-1], dtype=np.float32)
+    for i in range(n - 1, -1, -1):
+        acc = f32(acc + prod[..., i])
+    out.append(acc)
+    t = prod
+    while t.shape[-1] > 1:
+        t = f32(t[..., 0::2] + t[..., 1::2])
+    out.append(t[..., 0])
+    part = np.zeros(prod.shape[:-1] + (16,), dtype=np.float32)
+    for i in range(0, n, 16):
+        part = f32(part + prod[..., i:i + 16])
+    acc = np.zeros(prod.shape[:-1], dtype=np.float32)
+    for r in range(16):
+        acc = f32(acc + part[..., r])
+    out.append(acc)
+    out.append(prod.sum(axis=-1, dtype=np.float32))
+    return out
+
+
+@pytest.mark.parametrize("code,D,outliers", [("e4m3", 256, True), ("e4m3", 128, False),
+                                             ("i8", 128, True), ("i8", 64, False)])
+def test_logit_bound_holds_in_fp32_orders(code, D, outliers):
+    P = problem(D=D, S=512, code=code, outliers=outliers)
+    rows, cols = np.arange(128, 256), np.arange(0, 512)
+    sm32 = f32(P.sm_scale)
+    n = 0
+    # 16-bit logits: products of 16-bit values are exact in fp32
+    prod16 = f32(P.q[0, 0][rows][:, None, :] * P.k[0, 0][cols][None, :, :])
+    s16 = A.logits16(P, 0, 0, rows, cols)
+    e16 = A._err_logits(P, 0, 0, rows, cols, s16, np.ones(s16.shape, bool))
+    for acc in sum_orders(prod16):
+        got = f32(acc * sm32).astype(np.float64)
+        assert (np.abs(got - s16) <= e16).all()
+        n += got.size
+    # 8-bit logits: e4m3 products exact in fp32, int8 accumulators exact;
+    # the scale product sQ * sK * sm in fp32, then one multiply
+    qv, kv = P.qv[0, 0][rows], P.kv[0, 0][cols]
+    sq = f32(P.q_scales[0, 0][rows // 128])
+    sk = f32(P.k_scales[0, 0][cols // 64])
+    c = f32(f32(sq[:, None] * sk[None, :]) * sm32)
+    s8 = A.logits8(P, 0, 0, rows, cols)
+    e8 = A._err_logits(P, 0, 0, rows, cols, s8, np.zeros(s8.shape, bool))
+    accs = sum_orders(f32(qv[:, None, :] * kv[None, :, :])) if code == "e4m3" else \
+        [f32(A.int_acc_exact(P, 0, 0, rows, cols).astype(np.float64))]
+    for acc in accs:
+        got = f32(acc * c).astype(np.float64)
+        assert (np.abs(got - s8) <= e8).all()
+        n += got.size
+    assert n >= 1e5
+
+
+def test_tilemix_bound_holds_for_fp32_shifted_exponents():
+    # exponent s - m of the int8 tiles evaluated the kernel's way in fp32
+    # (scale cut to 21 bits, integer reference, one rounding) and of the
+    # 16-bit tiles (fp32 dot in any order, one fma) stays within the bound
+    P = problem(D=128, S=512, code="i8", outliers=True, adaptive=False, exp8=False, f16=0.5)
+    rows = np.arange(384, 512)
+    s, r8, ok = A.routed_logits(P, 0, 0, rows)
+    m = np.where(ok, s, -np.inf).max(axis=1)
+    E = A._err_logits_tilemix(P, 0, 0, rows, np.arange(P.S_k), s, r8, m)
+    L2E = f32(1.4426950408889634)
+    ref = np.ceil(m * 1.4426950408889634)             # an integer reference (base 2)
+    cols = np.arange(P.S_k)
+    sm32 = f32(P.sm_scale)
+    acc = A.int_acc_exact(P, 0, 0, rows, cols).astype(np.float64)
+    sq = f32(P.q_scales[0, 0][rows // 128])[:, None]
+    sk = f32(P.k_scales[0, 0][cols // 64])[None, :]
+    c8 = f32(f32(f32(sq * sk) * sm32) * L2E)
+    c8 = ((c8.view(np.uint32) + np.uint32(4)) & np.uint32(0xFFFFFFF8)).view(np.float32)
+    y8 = f32(acc * c8.astype(np.float64) - ref[:, None])
+    prod = f32(P.q[0, 0][rows][:, None, :] * P.k[0, 0][cols][None, :, :])
+    c16 = f32(sm32 * L2E)
+    n = 0
+    for dot in sum_orders(prod):
+        y16 = f32(dot.astype(np.float64) * c16 - ref[:, None])
+        y = np.where(r8, y8, y16).astype(np.float64) / 1.4426950408889634
+        exact = s - ref[:, None] / 1.4426950408889634
+        assert (np.abs(y - exact)[ok] <= E[ok]).all()
+        n += int(ok.sum())
+    assert n >= 1e5
+
+
+# ---------------------------------------------------------------------------
+# (2) the bounds are small enough to check something
+# ---------------------------------------------------------------------------
+
+def test_bounds_not_vacuous_on_adaptive_workload():
+    # the adaptive workload's recipe (head dim 256, x20 outlier channels, a
+    # sink key, e4m3 logits and exponentials, tau = 4) on a shorter sequence
+    P = problem(D=256, S=1024, code="e4m3", outliers=True, Hq=2, Hkv=1)
+    n_dec = n_split = 0
+    ext = []
+    for h in range(2):
+        res, rows, usb = A.attn_lamp(P, 0, h, np.arange(0, 32, 3))
+        for brs in res.branches:
+            pr = brs[0]
+            dec = np.isfinite(pr.margin)
+            n_dec += int(dec.sum())
+            n_split += int(pr.dontcare.sum())
+            assert np.nanmax(pr.bound) < 0.05                # natural-log units
+        ext.append(res.extra_tol.max())
+        assert res.lse_tol.max() < 0.05
+    assert n_dec > 150
+    assert n_split <= 0.05 * n_dec
+    assert max(ext) < 0.5 * compare.ATOL["bf16"]
+
+
+def test_tilemix_lse_bound_small_on_normal_inputs():
+    P = problem(D=128, S=1024, code="i8", outliers=False, adaptive=False, exp8=False, f16=0.25)
+    _, _, lse_tol = A.tilemix_bounds(P, 0, 1, np.arange(1024))
+    assert lse_tol.max() < 5e-3
+
+
+# ---------------------------------------------------------------------------
+# (3) every fp32 evaluation within the bounds is accepted
+# ---------------------------------------------------------------------------
+
+def fake_gpu(rng, edge):
+    """Offsets within the bound: uniform, or at +-0.999 of it (edge)."""
+    def perturb(e):
+        if edge:
+            return np.where(rng.random(e.shape) < 0.5, -0.999, 0.999) * e
+        return rng.uniform(-0.999, 0.999, e.shape) * e
+    return perturb
+
+
+def near_threshold_tau(P, h, sbs):
+    """A tau that puts one mid-sequence flag decision exactly on the
+    threshold, so that the oracle must evaluate it both ways."""
+    res, _, _ = A.attn_lamp(P, 0, h, sbs)
+    # a decision on a tile that raises no row's running maximum (its margin
+    # is below tau; where some row's maximum rises, max(s8 - m') is 0)
+    mg = np.concatenate([brs[0].margin for brs in res.branches])
+    cand = np.sort(mg[np.isfinite(mg) & (mg < P.tau - 0.5)])
+    assert cand.size
+    return P.tau - cand[len(cand) // 2]
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("kind", ["adaptive_e4m3", "adaptive_i8", "exp8_only"])
+def test_perturbed_within_bound_is_accepted(kind, seed):
+    rng = np.random.default_rng(100 + seed)
+    code = "i8" if kind == "adaptive_i8" else "e4m3"
+    P = problem(D=128, S=640, code=code, outliers=(seed % 2 == 0 or seed >= 3),
+                adaptive=(kind != "exp8_only"),
+                f16=0.3 if kind == "exp8_only" else 0.0, seed=seed)
+    sbs = np.arange(0, 20)
+    if P.adaptive and seed >= 3:
+        P.tau = near_threshold_tau(P, 1, sbs)
+    for h in range(P.Hq):
+        res, rows, usb = A.attn_lamp(P, 0, h, sbs)
+        if P.adaptive and seed >= 3 and h == 1:
+            assert res.flag_dontcare.any()
+        for edge in (False, True):
+            fake, rows2, usb2 = A.attn_lamp(P, 0, h, sbs, perturb=fake_gpu(rng, edge))
+            assert (rows2 == rows).all() and (usb2 == usb).all()
+            # flags differ only where the oracle took the decision both ways
+            first = np.argmax(fake.flags != res.flags, axis=1)
+            diff = (fake.flags != res.flags).any(axis=1)
+            assert res.flag_dontcare[np.flatnonzero(diff), first[diff]].all()
+            st = compare.check_lamp(res, fake.O, "bf16",
+                                    flags_gpu=fake.flags if P.adaptive else None,
+                                    lse_gpu=fake.lse)
+            assert st["ok"], st
+
+
+@pytest.mark.parametrize("edge", [False, True])
+def test_perturbed_within_bound_is_accepted_adaptive_workload_shape(edge):
+    # head dim 256, x20 outlier channels and a sink: even with every logit
+    # off by 99.9% of its worst-case bound the output stays within the
+    # spec tolerance of the branch the flags pick
+    rng = np.random.default_rng(11)
+    P = problem(D=256, S=1024, code="e4m3", outliers=True, adaptive=True, f16=0.0, seed=5)
+    sbs = np.arange(0, 32, 3)
+    for h in range(P.Hq):
+        res, _, _ = A.attn_lamp(P, 0, h, sbs)
+        fake, _, _ = A.attn_lamp(P, 0, h, sbs, perturb=fake_gpu(rng, edge))
+        st = compare.check_lamp(res, fake.O, "bf16", flags_gpu=fake.flags, lse_gpu=fake.lse)
+        assert st["ok"], st
+
+
+def test_perturbed_tilemix_lse_within_bound():
+    rng = np.random.default_rng(7)
+    P = problem(D=128, S=768, code="i8", outliers=True, adaptive=False, exp8=False, f16=0.3,
+                scale=3.0)
+    rows = np.arange(P.S_q)
+    O, lse, lse_tol = A.tilemix_bounds(P, 0, 0, rows)
+    s, r8, ok = A.routed_logits(P, 0, 0, rows)
+    m = np.where(ok, s, -np.inf).max(axis=1)
+    E = A._err_logits_tilemix(P, 0, 0, rows, np.arange(P.S_k), np.where(ok, s, 0), r8, m)
+    for _ in range(4):
+        sp = np.where(ok, s + rng.uniform(-0.999, 0.999, s.shape) * E, -np.inf)
+        mp = sp.max(axis=1)
+        lsep = mp + np.log(np.exp(sp - mp[:, None]).sum(axis=1))
+        assert (np.abs(lsep - lse) <= lse_tol).all()
+
+
+# ---------------------------------------------------------------------------
+# flags grow with tau when the 8-bit logits equal the 16-bit ones
+# ---------------------------------------------------------------------------
+
+def test_flags_first_tile_and_monotone_in_tau_exact_logits():
+    # Q, K = 2^-7 times integers in [-127, 127] with one +-127 * 2^-7 per
+    # quantisation block: the int8 scale is exactly 2^-7 and the codes are
+    # the integers, so the 8-bit logits equal the 16-bit ones, the running
+    # maximum does not depend on the flags, and the flag set can only grow
+    # with tau
+    rng = np.random.default_rng(3)
+    S, D = 384, 32
+    qi = rng.integers(-127, 128, (1, 1, S, D))
+    ki = rng.integers(-127, 128, (1, 1, S, D))
+    qi[:, :, ::64, 0] = 127
+    ki[:, :, ::64, 0] = -127
+    q, k = qi * 2.0 ** -7, ki * 2.0 ** -7
+    v = rng.standard_normal((1, 1, S, D))
+    prev = None
+    for tau in (0.0, 0.25, 0.5, 1.0, 2.0, 4.0, 8.0):
+        P = A.make_problem(q, k, v, causal=True, code="i8", tile_m=64, tile_n=64,
+                           tiles_per_bit=1, frac_16bit=0.0, seed=1, adaptive=True, exp8=False,
+                           tau=tau, sub_rows=32, sm_scale=0.05)
+        assert (P.q_scales == np.float32(2.0 ** -7)).all()
+        assert np.abs(A.logits8(P, 0, 0, np.arange(S), np.arange(S)) -
+                      A.logits16(P, 0, 0, np.arange(S), np.arange(S))).max() == 0
+        res, rows, usb = A.attn_lamp(P, 0, 0, np.arange(S // 32))
+        assert res.flags[:, 0].all()              # every row's first tile
+        if prev is not None:
+            assert (res.flags | ~prev).all()      # nothing unflagged as tau grows
+            assert res.flags.sum() >= prev.sum()
+        prev = res.flags
+    assert 0 < prev.mean() < 1
