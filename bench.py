@@ -224,6 +224,36 @@ def decode_measurement(torch, L, iters=20, warmup=3):
             "workspace_bytes": int(ws.numel())}
 
 
+def profile_suite(torch, L, steps, warmup):
+    """Each benchmarked configuration's step (quantisers, mask builder,
+    attention) run warmup + steps times, in a fixed order, then the decode
+    step: one process whose kernel dispatches a profiler can attribute by
+    order.  Returns the per-configuration mean attention time."""
+    from synthetic import get_config, make_inputs
+    dev = torch.device("cuda:0")
+    out = {}
+    runs = [("C5", 0.25, "i8", False), ("C5", 0.25, "e4m3", False), ("C5", 0.25, "e4m3", True),
+            ("C4", None, None, False), ("C3", None, None, False)]
+    cache = {}
+    for name, f, code, pv8 in runs:
+        cfg = get_config(name, f, code)
+        if name not in cache:
+            cache.clear()
+            q, k, v = make_inputs(cfg)
+            cache[name] = tuple(t.to(dev) for t in (q, k, v))
+            del q, k, v
+        qd, kd, vd = cache[name]
+        pipe = Pipeline(L, cfg, qd, kd, vd, torch, pv8=pv8)
+        ts = time_attn(torch, pipe, iters=steps, warmup=warmup, prep_each=True)
+        key = cfg.name + ("_pv8" if pv8 else "")
+        out[key] = round(float(np.mean(ts)) * 1e3, 4)
+        log(f"[bench] profile suite: {key} attention {out[key]} ms")
+        del pipe
+    cache.clear()
+    out["decode"] = decode_measurement(torch, L, iters=steps, warmup=warmup)["ms_mean"]
+    return out
+
+
 # ---------------------------------------------------------------------------
 # traffic from the committed rocprofv3 counter summary of this kernel
 # ---------------------------------------------------------------------------
@@ -244,10 +274,31 @@ def committed_traffic(workload):
 # CPU oracle baseline (bounded sample of the same workload)
 # ---------------------------------------------------------------------------
 
+def host_description():
+    """CPU model (from /proc/cpuinfo) and the BLAS library numpy uses."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        b = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas = f"{b.get('name')} {b.get('version')}".strip()
+    except Exception:
+        pass
+    return model, blas
+
+
 def cpu_baseline(cfg, q, k, v, budget_s=12.0):
     from oracle import attention as A
     from oracle import mask as omask
     cores = len(os.sched_getaffinity(0))
+    cpu_model, blas = host_description()
     t_prep = 0.0
     dt = 0.0
     flops = 0.0
@@ -291,6 +342,7 @@ def cpu_baseline(cfg, q, k, v, budget_s=12.0):
                 break
         dt += time.perf_counter() - t1
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model, "blas": blas,
             "sample": (f"numpy fp64 oracle, {tiles} query tiles of {cfg.tile_m} rows over {heads} "
                        f"head(s) from (b=0, h=0), each head's tiles from the longest down "
                        f"({tiles * cfg.tile_m} of {cfg.B * cfg.Hq * cfg.S} query rows of the "
@@ -433,12 +485,21 @@ def component_times(torch, pipe, iters=20):
     return out
 
 
-def time_attn(torch, pipe, iters, warmup):
+def time_attn(torch, pipe, iters, warmup, prep_each=False):
+    """Attention launch times (HIP events around each launch); prep_each:
+    the quantisers and the mask builder run before every launch as well
+    (outside the events)."""
+    if not prep_each:
+        pipe.prep()
     for _ in range(warmup):
+        if prep_each:
+            pipe.prep()
         pipe.attn()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(iters)]
     for a, b in ev:
+        if prep_each:
+            pipe.prep()
         a.record()
         pipe.attn()
         b.record()
@@ -462,6 +523,9 @@ def main():
                          "dispatch for scaling the HBM byte counters)")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode measurement over an int8 K/V cache (for profiling)")
+    ap.add_argument("--profile-suite", action="store_true",
+                    help="only run --steps steps of every benchmarked kernel configuration, one "
+                         "after the other (for rocprofv3 counter passes)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -476,6 +540,10 @@ def main():
 
     if args.decode_only:
         print(json.dumps({"decode_int8_kv": decode_measurement(torch, L)}), flush=True)
+        return
+    if args.profile_suite:
+        print(json.dumps({"profile_suite": profile_suite(torch, L, args.steps, args.warmup)}),
+              flush=True)
         return
 
     cfg = get_config(args.config, args.frac, args.code)

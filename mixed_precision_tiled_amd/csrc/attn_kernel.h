@@ -465,7 +465,12 @@ void attn_fwd_kernel(const AttnArgs a) {
     if (is8) {
       qk8_lds(ADAPTIVE ? kb8 : kb, key0, x);
       lg.c = (sQ * sK) * sm * kLogScale;
-      if constexpr (LAZY && !E4M3) lg.xoff = kMagic;
+      if constexpr (LAZY && !E4M3) {
+        // 21 significant bits make kMagic * c exact, so that the offset can
+        // be folded into the reference without a rounding
+        lg.c = round_sig21(lg.c);
+        lg.xoff = kMagic;
+      }
     } else {
       qk16_lds(kb, x);
       lg.c = sm * kLogScale;
@@ -578,8 +583,25 @@ void attn_fwd_kernel(const AttnArgs a) {
     // their sum
     auto weights = [&](float mref) -> float {
       if constexpr (LAZY) {
-        // exp2((x - xoff) * cm - m) with the offset folded into the constant
-        const float msub = ((mref == kNegInf) ? 0.f : mref) + xoff * cm;
+        // exp2((x - xoff) * cm - m) as exp2(x * cm - (m + xoff * cm)), one
+        // rounding, when m + xoff * cm is exact in fp32: xoff * cm is exact
+        // (cm has 21 significant bits) and the reference m is an integer, so
+        // the sum is exact whenever its magnitude stays near xoff * cm's.
+        // The rounding error of the sum (TwoSum) says which: otherwise the
+        // offset is subtracted from each x first (exact: x = xoff + acc with
+        // |acc| < 2^22), again one rounding per weight.
+        const float mr = (mref == kNegInf) ? 0.f : mref;
+        const float t = xoff * cm;
+        float msub = mr + t;
+        const float bb = msub - mr;
+        const float err = (mr - (msub - bb)) + (t - bb);
+        if (wave_any(err != 0.f)) {
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int e = 0; e < 32; ++e) x[e] -= xoff;
+          msub = mr;
+          __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int e = 0; e < 32; ++e) x[e] = exp2_fast(__builtin_fmaf(x[e], cm, -msub));
       } else {
@@ -635,8 +657,10 @@ void attn_fwd_kernel(const AttnArgs a) {
     bool move;
     float m_new;
     if constexpr (LAZY) {
+      // the reference stays an integer (base-2 units), which keeps the
+      // folded offset exact and makes alpha an exact power of two
       move = wave_any(mx > m_run + 8.f);
-      m_new = move ? fmaxf(m_run, mx) : m_run;
+      m_new = move ? ceilf(fmaxf(m_run, mx)) : m_run;
     } else {
       m_new = fmaxf(m_run, mx);
       move = wave_any(m_new != m_run);

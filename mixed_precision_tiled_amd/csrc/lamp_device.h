@@ -143,6 +143,13 @@ __device__ __forceinline__ float sum16x2(uint32_t v, float c) {
 constexpr int kMagicBits = 0x4B400000;
 constexpr float kMagic = 12582912.0f;   // 1.5 * 2^23
 
+// c >= 0 rounded to 21 significant bits (ties away from zero).  kMagic * c is
+// then exact in fp32: 3 * c needs at most 23 significant bits and 2^22 only
+// moves the exponent.  The relative change of c is at most 2^-21.
+__device__ __forceinline__ float round_sig21(float c) {
+  return __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, c) + 4u) & ~7u);
+}
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------

@@ -33,6 +33,7 @@ class Config:
     mask_seed: int = 0
     mask_all_ones: bool = False   # adaptive config routes every tile 8-bit first
     sm_scale: float = 0.0         # <= 0 -> 1/sqrt(D)
+    input_scale: float = 1.0      # Q and K multiplied by this (fp32, before the cast)
 
     @property
     def n_qt(self):

@@ -9,6 +9,9 @@ and a sign per channel from the same generator; Q's outlier channels become
 20 * sign * |Q|, K's become 20 * K, and key 0 of every (batch, KV head) gets
 40 * sign on the outlier channels (an attention sink every query sees).  The
 scaling happens in fp32 before the cast.
+
+Input scale (optional): Q and K are multiplied by a constant in fp32 after
+the outlier step and before the cast, for cases with large logits.
 """
 import torch
 
@@ -30,5 +33,8 @@ def make_inputs(cfg, seed=None, S=None):
         q[..., ch] = 20.0 * sign * q[..., ch].abs()
         k[..., ch] = 20.0 * k[..., ch]
         k[:, :, 0, ch] = 40.0 * sign
+    if cfg.input_scale != 1.0:
+        q = q * cfg.input_scale
+        k = k * cfg.input_scale
     dt = _DT[cfg.dtype]
     return q.to(dt), k.to(dt), v.to(dt)

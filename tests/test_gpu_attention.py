@@ -2,9 +2,11 @@
 
 * small multi-tile cases with ragged tails, every head dim, both tile heights,
   fp16 and bf16, int8 and e4m3, causal and not: every output element;
-* the Lamp variants (8-bit exponentials, adaptive flags): every element, with
-  the per-row widening for possible e4m3 rounding flips and rows whose flag
-  decision lies within the GPU error bound excluded (counted);
+* the Lamp variants (8-bit exponentials, adaptive flags): every element; a
+  flag decision within the GPU error bound of the threshold is evaluated both
+  ways by the oracle and the GPU's flags pick the branch (no row is
+  excluded), and the tolerance is widened by the bound for e4m3 rounding
+  flips and fp32 exponent errors;
 * the five workload configurations at full size, in the launch configuration
   the benchmark uses, on sampled query tiles the oracle computes row by row;
 * int32 QK^T accumulators bit-exact; invariants (V = 1 gives O = 1); empty
@@ -16,7 +18,9 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import device, gpu_run, oracle_mask, oracle_problem, u64
+import zlib
+
+from gpu_util import device, gpu_run, oracle_mask, oracle_problem, record_lamp, u64
 from oracle import attention as A
 from oracle import compare
 from oracle import mask as omask
@@ -24,29 +28,29 @@ from synthetic import CONFIGS, Config, c5_variant, make_inputs
 
 pytestmark = pytest.mark.gpu
 
-# Rows whose adaptive flag decision lies within the rigorous fp32 error bound
-# of the threshold are excluded from pass/fail (their count is printed); the
-# bound is worst-case (gamma_D times the sum of |products|), so with D = 256
-# and x20 outlier channels a few 32-row sub-blocks per head fall inside it.
-MAX_FRAGILE = 0.10
-
-
 def L():
     import mixed_precision_tiled_amd as lamp
     return lamp
 
 
 def small_cfg(D, tm, dtype, code, causal, B, Hq, Hkv, S, G, f16, exp8=False, adaptive=False,
-              outliers=False, seed=7, tau=4.0):
+              outliers=False, seed=7, tau=4.0, input_scale=1.0):
     return Config(f"small_d{D}_m{tm}", B=B, Hq=Hq, Hkv=Hkv, S=S, D=D, causal=causal, dtype=dtype,
                   tile_m=tm, tile_n=64, tiles_per_bit=G, frac_16bit=f16, code=code, exp8=exp8,
                   adaptive=adaptive, tau=tau, outliers=outliers, input_seed=seed,
-                  mask_seed=seed + 1000)
+                  mask_seed=seed + 1000, input_scale=input_scale)
 
 
 def inputs_qk(cfg, S_q, S_k):
     q, k, v = make_inputs(cfg, S=max(S_q, S_k))
     return (q[:, :, :S_q].contiguous(), k[:, :, :S_k].contiguous(), v[:, :, :S_k].contiguous())
+
+
+def check_lse(lg, lse_ref, lse_tol):
+    none = np.isneginf(lse_ref)
+    assert np.isneginf(lg[none]).all() and np.isfinite(lg[~none]).all()
+    d = np.abs(lg[~none] - lse_ref[~none])
+    assert (d <= lse_tol[~none]).all(), f"LSE off by {d.max()} (bound {lse_tol[~none].min()})"
 
 
 def check_head(cfg, P, g, b, h, rows=None, sub_blocks=None, report=None):
@@ -57,43 +61,29 @@ def check_head(cfg, P, g, b, h, rows=None, sub_blocks=None, report=None):
     if A.uses_lamp(P):
         if sub_blocks is None:
             sub_blocks = np.arange(-(-P.S_q // P.sub_rows))
-        res, rr, usb = A.attn_lamp(P, pb, ph, sub_blocks)
-        st = compare.check(got[rr], res.O, cfg.dtype, extra_row=res.extra_tol,
-                           exclude_rows=res.fragile_rows)
-        if report is not None and res.fragile_rows.any():
-            fe = float(np.abs(got[rr][res.fragile_rows] - res.O[res.fragile_rows]).max())
-            report["fragile_max_err"] = max(report.get("fragile_max_err", 0.0), fe)
-        lse_ref, lse_rows = res.lse, rr
+        res, rr, usb = A.attn_lamp(P, pb, ph, sub_blocks, dtype=cfg.dtype)
+        gflags = None
         if P.adaptive and g["flags"] is not None:
-            n_kt = P.n_kt
-            gbits = omask.unpack_bits(g["flags"][b, h], g["flags"].shape[-1] * 64)[:, :n_kt]
-            gsel = gbits[usb].astype(bool)
-            mism = (gsel != res.flags) & ~res.flag_dontcare
-            assert not mism.any(), f"flags differ at {np.argwhere(mism)[:5]}"
-            # bits beyond n_kt are zero
             allbits = omask.unpack_bits(g["flags"][b, h], g["flags"].shape[-1] * 64)
-            assert not allbits[:, n_kt:].any()
-            if report is not None:
-                report["flag_frac"] = report.get("flag_frac", []) + [float(res.flags.mean())]
-                report["dontcare"] = report.get("dontcare", 0) + int(res.flag_dontcare.sum())
+            assert not allbits[:, P.n_kt:].any()            # bits beyond n_kt are zero
+            gflags = allbits[usb][:, :P.n_kt].astype(bool)
+        glse = None if g["lse"] is None else g["lse"][b, h][rr]
+        st = compare.check_lamp(res, got[rr], cfg.dtype, flags_gpu=gflags, lse_gpu=glse)
+        record_lamp(st)
         if report is not None:
-            report["fragile_rows"] = report.get("fragile_rows", 0) + int(res.fragile_rows.sum())
-            report["rows"] = report.get("rows", 0) + len(rr)
+            for k in ("n_subblocks", "n_split", "n_nonprimary", "flag_mismatch", "n_bad"):
+                report[k] = report.get(k, 0) + st[k]
+            report["max_extra"] = max(report.get("max_extra", 0.0), st["max_extra"])
+            if P.adaptive:
+                report["flag_frac"] = report.get("flag_frac", []) + [round(float(res.flags.mean()), 4)]
+        assert st["ok"], f"head ({b},{h}): {st}"
     else:
         rr = np.arange(P.S_q) if rows is None else np.asarray(rows)
-        O, lse_ref = A.attn_tilemix(P, pb, ph, rr)
+        O, lse_ref, lse_tol = A.tilemix_bounds(P, pb, ph, rr, cfg.dtype)
         st = compare.check(got[rr], O, cfg.dtype)
-        lse_rows = rr
-    assert st["ok"], f"head ({b},{h}): {st}"
-    if g["lse"] is not None:
-        # the kernel's normaliser sums the 16-bit-rounded weights that also
-        # feed P V, so its log can be off by ln(1 + u16) (u16 = 2^-8 for
-        # bf16, 2^-11 for fp16) on top of fp32 rounding
-        u16 = 2.0 ** -8 if cfg.dtype == "bf16" else 2.0 ** -11
-        lg = g["lse"][b, h][lse_rows]
-        assert np.isfinite(lg).all()
-        assert np.abs(lg - lse_ref).max() <= 1e-3 + u16 + 1e-5 * np.abs(lse_ref).max() + (
-            0.05 if A.uses_lamp(P) else 0.0)
+        assert st["ok"], f"head ({b},{h}): {st}"
+        if g["lse"] is not None:
+            check_lse(g["lse"][b, h][rr], lse_ref, lse_tol)
     return st
 
 
@@ -182,6 +172,33 @@ def test_small_tilemix(case):
             check_head(cfg, P, g, b, h)
 
 
+# int8 tiles under mask routing with full-precision exponentials, on inputs
+# with four outlier channels and a sink key: large, tile-dependent scales must
+# not bias the weights of a key tile.  With Q and K also scaled x10 the
+# logits reach ~3e4, where any fp32 evaluation of a per-tile scale already
+# moves the weights of different key tiles apart by ~1e-3 relative, beyond
+# the fp16 bound of 2e-3 on O in rows whose top keys compete; that stress
+# runs in bf16 only
+INT8_OUTLIERS = [(D, dt, f16, 1.0) for D in (128, 256) for dt in ("bf16", "f16")
+                 for f16 in (0.0, 0.25)] + [(D, "bf16", f16, 10.0) for D in (128, 256)
+                                            for f16 in (0.0, 0.25)]
+
+
+@pytest.mark.parametrize("case", INT8_OUTLIERS,
+                         ids=lambda c: "d{}_{}_f{}_x{}".format(c[0], c[1], c[2], int(c[3])))
+def test_int8_outliers(case):
+    D, dt, f16, sc = case
+    cfg = small_cfg(D, 128, dt, "i8", True, 1, 2, 1, 2048, 4, f16, outliers=True, seed=31,
+                    input_scale=sc)
+    q, k, v = make_inputs(cfg)
+    print(f"[attn] int8 outliers {case}", flush=True)
+    g = gpu_run(cfg, q, k, v)
+    P = oracle_problem(cfg, q, k, v)
+    check_codes_and_mask(cfg, P, g)
+    for h in range(cfg.Hq):
+        check_head(cfg, P, g, 0, h)
+
+
 LAMP = [
     # D, tm, dtype, code, causal, B, Hq, Hkv, S_q, S_k, G, f16, exp8, adaptive, outliers
     (128, 128, "bf16", "e4m3", True, 1, 2, 1, 320, 320, 1, 0.3, True, False, False),
@@ -212,7 +229,6 @@ def test_small_lamp(case):
         for h in range(Hq):
             check_head(cfg, P, g, b, h, report=rep)
     print(f"  lamp report {rep}", flush=True)
-    assert rep.get("fragile_rows", 0) <= MAX_FRAGILE * rep["rows"]
 
 
 # 8-bit P V on 8-bit tiles (exp8, mask routing): e4m3 weights times
@@ -248,7 +264,6 @@ def test_small_pv8(case):
         for h in range(Hq):
             check_head(cfg, P, g, b, h, report=rep)
     print(f"  pv8 report {rep}", flush=True)
-    assert rep.get("fragile_rows", 0) <= MAX_FRAGILE * rep["rows"]
 
 
 # ---------------------------------------------------------------------------
@@ -261,25 +276,32 @@ def cached_inputs(name, seed):
     return make_inputs(cfg, seed=seed)
 
 
-FULL = [("C2", None, None), ("C3", None, None), ("C4", None, None),
-        ("C5", 0.25, "i8"), ("C5", 0.0, "i8"), ("C5", 1.0, "i8"), ("C5", 0.10, "e4m3"),
-        ("C5", 0.50, "e4m3")]
+# every line the benchmark times: C2-C4 as configured, the C5 sweep (five
+# 16-bit fractions x both 8-bit codes) and the C5 8-bit P V lines
+FULL = [("C2", None, None, False), ("C3", None, None, False), ("C4", None, None, False)] + \
+    [("C5", f, c, False) for c in ("i8", "e4m3") for f in (0.0, 0.10, 0.25, 0.50, 1.0)] + \
+    [("C5", 0.0, "e4m3", True), ("C5", 0.25, "e4m3", True)]
 
 
-@pytest.mark.parametrize("name,f16,code", FULL, ids=lambda x: str(x))
-def test_full_config_sampled(name, f16, code):
+@pytest.mark.parametrize("name,f16,code,pv8", FULL, ids=lambda x: str(x))
+def test_full_config_sampled(name, f16, code, pv8):
     cfg = CONFIGS[name] if f16 is None else c5_variant(f16, code)
     q, k, v = cached_inputs(name, cfg.input_seed)
-    print(f"[attn] full {cfg.name}", flush=True)
-    g = gpu_run(cfg, q, k, v)
+    print(f"[attn] full {cfg.name}{' pv8' if pv8 else ''}", flush=True)
+    g = gpu_run(cfg, q, k, v, pv8=pv8)
     assert np.isfinite(g["out"]).all()
     mw = oracle_mask(cfg, cfg.S, cfg.S)
     assert (g["mask"] == mw).all()
-    rng = np.random.default_rng(hash(cfg.name) % 2 ** 32)
+    rng = np.random.default_rng(zlib.crc32(cfg.name.encode()))
     heads = [(0, 0), (cfg.B - 1, cfg.Hq - 1), (int(rng.integers(cfg.B)), int(rng.integers(cfg.Hq)))]
     rep = {}
     for b, h in heads:
-        P = oracle_problem(cfg, q, k, v, b=b, h=h, mask_words=mw)
+        P = oracle_problem(cfg, q, k, v, b=b, h=h, mask_words=mw, pv8=pv8)
+        if pv8:
+            from oracle import quant as oq
+            kvh = h // (cfg.Hq // cfg.Hkv)
+            assert (g["v8"][b, kvh] == oq.pack_v_tiles(P.v_codes)[0, 0]).all()
+            assert (g["vs"][b, kvh] == P.v_scales[0, 0]).all()
         qts = sorted({0, cfg.n_qt - 1, int(rng.integers(cfg.n_qt))})
         if A.uses_lamp(P):
             per = cfg.tile_m // cfg.sub_rows
@@ -291,7 +313,6 @@ def test_full_config_sampled(name, f16, code):
             check_head(cfg, P, g, b, h, rows=rows)
     if rep:
         print(f"  lamp report {rep}", flush=True)
-        assert rep.get("fragile_rows", 0) <= MAX_FRAGILE * rep["rows"]
 
 
 # ---------------------------------------------------------------------------
@@ -455,32 +476,27 @@ def test_varlen(case):
     assert (k8.cpu().numpy() == P.k_codes).all() and (sk.cpu().numpy() == P.k_scales).all()
     got, glse = out.float().cpu().numpy(), lse.cpu().numpy()
     gflags = None if flags is None else u64(flags)
-    u16 = 2.0 ** -8 if dt == "bf16" else 2.0 ** -11
     for b in range(B):
         if Lq[b] == 0:
             continue
         for h in range(Hq):
             if A.uses_lamp(P):
                 nsb = -(-Lq[b] // 32)
-                res, rr, usb = A.attn_lamp(P, b, h, np.arange(nsb))
+                res, rr, usb = A.attn_lamp(P, b, h, np.arange(nsb), dtype=dt)
                 keep = rr < Lq[b]
-                rows, O_ref, lse_ref = rr[keep], res.O[keep], res.lse[keep]
-                st = compare.check(got[b, h][rows], O_ref, dt, extra_row=res.extra_tol[keep],
-                                   exclude_rows=res.fragile_rows[keep])
+                fl = None
                 if ad:
-                    n_kt = P.n_kt
-                    gb = omask.unpack_bits(gflags[b, h], gflags.shape[-1] * 64)[:, :n_kt]
-                    mism = (gb[usb].astype(bool) != res.flags) & ~res.flag_dontcare
-                    assert not mism.any()
+                    fl = omask.unpack_bits(gflags[b, h], gflags.shape[-1] * 64)[usb][:, :P.n_kt]
+                    fl = fl.astype(bool)
+                st = compare.check_lamp(res, got[b, h][rr], dt, flags_gpu=fl,
+                                        lse_gpu=glse[b, h][rr], keep=keep)
+                record_lamp(st)
+                rows, lse_ref = rr[keep], res.lse[keep]
             else:
                 rows = np.arange(Lq[b])
-                O_ref, lse_ref = A.attn_tilemix(P, b, h, rows)
+                O_ref, lse_ref, lse_tol = A.tilemix_bounds(P, b, h, rows, dt)
                 st = compare.check(got[b, h][rows], O_ref, dt)
+                check_lse(glse[b, h][rows], lse_ref, lse_tol)
             assert st["ok"], f"varlen ({b},{h}): {st}"
             none = np.isneginf(lse_ref)
-            lg = glse[b, h][rows]
-            assert np.isneginf(lg[none]).all() and (got[b, h][rows][none] == 0).all()
-            assert np.isfinite(lg[~none]).all()
-            assert np.abs(lg[~none] - lse_ref[~none]).max(initial=0) <= (
-                1e-3 + u16 + 1e-5 * np.abs(lse_ref[~none]).max(initial=0) +
-                (0.05 if A.uses_lamp(P) else 0.0))
+            assert (got[b, h][rows][none] == 0).all()

@@ -33,6 +33,9 @@ CASES = [
     (128, "bf16", 1, 4, 1, 8, 64, True, 128),        # 32 columns, one tile
     (128, "f16", 1, 2, 2, 3, 1, False, 64),          # a one-key cache
     (64, "bf16", 3, 16, 2, 2, 4097, True, 64),       # more than one split, ragged last split
+    # the benchmarked step: batch 8, Qwen3-8B heads, one new token over a
+    # 32768-token cache (32-tile splits, 16 per (batch, KV head))
+    (128, "bf16", 8, 32, 8, 1, 32768, True, 64),
 ]
 
 
