@@ -562,13 +562,20 @@ void attn_fwd_kernel(const AttnArgs a) {
   //     products are then spread over the softmax arithmetic.
   auto softmax_part = [&](float* x, const Logits& lg, uint32_t* pk, auto pvc) {
     constexpr bool WITH_PV = decltype(pvc)::value;
+    // LAZY after the first tile: the weights are taken against the current
+    // reference and the row maximum is only needed when they grow too large
+    // (WITH_PV holds exactly on the tiles after a row's first)
+    constexpr bool MAXFREE = LAZY && WITH_PV;
     const float cm = lg.scaled ? 1.f : lg.c;
-    const float xoff = lg.xoff;
-    float mx = x[0];
+    // offset still in x (cleared when it is subtracted from x in place)
+    float xo = lg.xoff;
+    auto row_max = [&]() {
+      float mx = x[0];
 #pragma unroll
-    for (int e = 1; e < 32; ++e) mx = fmaxf(mx, x[e]);
-    mx = (mx - xoff) * cm;
-    mx = halves_max(mx);
+      for (int e = 1; e < 32; ++e) mx = fmaxf(mx, x[e]);
+      mx = (mx - xo) * cm;
+      return halves_max(mx);
+    };
     // the normaliser sums exactly the rounded weights that feed P V
     auto psum = [&](const uint32_t* w16) {
       float ps0 = 0.f, ps1 = 0.f;
@@ -579,8 +586,8 @@ void attn_fwd_kernel(const AttnArgs a) {
       }
       return ps0 + ps1;
     };
-    // the weights go to pk (the fp32 weights overwrite x in place); returns
-    // their sum
+    // the weights go to pk (LAZY keeps x; otherwise the fp32 weights
+    // overwrite x in place); returns their sum
     auto weights = [&](float mref) -> float {
       if constexpr (LAZY) {
         // exp2((x - xoff) * cm - m) as exp2(x * cm - (m + xoff * cm)), one
@@ -591,19 +598,23 @@ void attn_fwd_kernel(const AttnArgs a) {
         // offset is subtracted from each x first (exact: x = xoff + acc with
         // |acc| < 2^22), again one rounding per weight.
         const float mr = (mref == kNegInf) ? 0.f : mref;
-        const float t = xoff * cm;
+        const float t = xo * cm;
         float msub = mr + t;
         const float bb = msub - mr;
         const float err = (mr - (msub - bb)) + (t - bb);
         if (wave_any(err != 0.f)) {
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int e = 0; e < 32; ++e) x[e] -= xoff;
+          for (int e = 0; e < 32; ++e) x[e] -= xo;
+          xo = 0.f;
           msub = mr;
           __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int e = 0; e < 32; ++e) x[e] = exp2_fast(__builtin_fmaf(x[e], cm, -msub));
+        for (int i = 0; i < 16; ++i)
+          pk[i] = pack16x2<BF16>(exp2_fast(__builtin_fmaf(x[2 * i], cm, -msub)),
+                                 exp2_fast(__builtin_fmaf(x[2 * i + 1], cm, -msub)));
+        return psum(pk);
       } else {
         const float msub = (mref == kNegInf) ? 0.f : mref;
         if (EXP8 && !lg.is16) {
@@ -654,6 +665,30 @@ void attn_fwd_kernel(const AttnArgs a) {
     // O and l and the update of m_run follow in a rare branch.  LAZY moves
     // the reference only when a row's max grows by more than 8 (so p <= 2^8
     // in between); the exact modes track the running maximum.
+    if constexpr (MAXFREE) {
+      // Weights against the current reference first.  A lane's weights are
+      // all at most their sum, so a sum up to 2^16 keeps every weight in
+      // range; above it (or before any reference exists) the row maximum
+      // moves the reference and the tile is weighted again.  The rescale
+      // applies to everything accumulated so far, P V of the previous tile
+      // included.
+      float l_add = weights(m_run);
+      asm volatile("" : "+v"(l_add));
+      interleave_pv_softmax();
+      if (wave_any((l_add > 65536.f) | (m_run == kNegInf))) {
+        __builtin_amdgcn_sched_barrier(0);
+        const float m_new = ceilf(fmaxf(m_run, row_max()));
+        l_add = weights(m_new);
+        const float alpha = (m_new == kNegInf) ? 1.f : exp2_fast(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < SH::ND; ++db) O[db] *= alpha;
+        m_run = m_new;
+      }
+      l_run += l_add;
+      return;
+    }
+    const float mx = row_max();
     bool move;
     float m_new;
     if constexpr (LAZY) {
