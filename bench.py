@@ -224,6 +224,20 @@ def decode_measurement(torch, L, iters=20, warmup=3):
             "workspace_bytes": int(ws.numel())}
 
 
+def copy_calibration(torch, mib):
+    """One device-to-device copy of mib MiB: the reference dispatch that
+    scales the HBM byte counters of a counter pass."""
+    if mib <= 0:
+        return
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device=torch.device("cuda:0"))
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: {n} bytes read + {n} bytes written")
+
+
 def profile_suite(torch, L, steps, warmup):
     """Each benchmarked configuration's step (quantisers, mask builder,
     attention) run warmup + steps times, in a fixed order, then the decode
@@ -542,8 +556,9 @@ def main():
         print(json.dumps({"decode_int8_kv": decode_measurement(torch, L)}), flush=True)
         return
     if args.profile_suite:
-        print(json.dumps({"profile_suite": profile_suite(torch, L, args.steps, args.warmup)}),
-              flush=True)
+        res = profile_suite(torch, L, args.steps, args.warmup)
+        copy_calibration(torch, args.copy_calibration)
+        print(json.dumps({"profile_suite": res}), flush=True)
         return
 
     cfg = get_config(args.config, args.frac, args.code)
@@ -703,15 +718,7 @@ def main():
         result["cpu_baseline"] = cpu_baseline(cfg, q, k, v, budget_s=args.cpu_budget)
     else:
         result["cpu_baseline"] = None
-    if args.copy_calibration > 0:
-        n = args.copy_calibration << 20
-        src = torch.ones(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"[bench] copy calibration: {n} bytes read + {n} bytes written")
-        del src, dst
+    copy_calibration(torch, args.copy_calibration)
     print(json.dumps(result), flush=True)
 
 

@@ -394,6 +394,8 @@ lamp_status lamp_attn_fwd(const lamp_attn_params* p, void* stream) {
 // decode over an int8 key/value cache
 // ---------------------------------------------------------------------------
 
+extern "C" {
+
 size_t lamp_decode_workspace_bytes(int64_t B, int64_t Hkv, int64_t S_k, int64_t D) {
   if (B < 0 || Hkv < 0 || S_k < 0 || D < 0) return 0;
   const int64_t n_kt = cdiv(S_k, 64);
@@ -468,3 +470,5 @@ lamp_status lamp_decode_fwd(const lamp_decode_params* p, void* workspace, size_t
   a.ws_ml = a.ws_o + nslot * a.D;
   return hip_status(lamp::launch_decode(a, static_cast<hipStream_t>(stream)), "decode launch");
 }
+
+}  // extern "C"

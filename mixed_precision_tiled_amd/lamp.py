@@ -263,6 +263,33 @@ def lamp_attn_fwd(q, k, v, q8, k8, q_scale, k_scale, mask, *, code, causal, tile
     for t in (seqlens_q, seqlens_k):
         if t is not None and (t.dtype != torch.int32 or tuple(t.shape) != (B,)):
             raise ValueError("seqlens must be int32 tensors [B]")
+    # shapes and dtypes of everything the kernel reads or writes (a
+    # mismatch would read or write out of bounds on the device)
+    n_qt, n_kt = cdiv(S_q, tile_m), cdiv(S_k, tile_n)
+
+    def need(name, t, shape, dtypes):
+        if tuple(t.shape) != tuple(shape) or t.dtype not in dtypes:
+            raise ValueError(f"{name}: expected shape {tuple(shape)} and dtype in "
+                             f"{[str(d) for d in dtypes]}, got {tuple(t.shape)} {t.dtype}")
+    codes = (torch.uint8, torch.int8)
+    need("q8", q8, (B, Hq, S_q, D), codes)
+    need("k8", k8, (B, Hkv, S_k, D), codes)
+    need("out", out, (B, Hq, S_q, D), (q.dtype,))
+    if tile_m in (64, 128) and tile_n == 64:
+        # (other tilings are refused by the library before any launch)
+        need("q_scale", q_scale, (B, Hq, n_qt), (torch.float32,))
+        need("k_scale", k_scale, (B, Hkv, n_kt), (torch.float32,))
+        need("mask", mask, (B, Hq, n_qt, W), (torch.int64, torch.uint64))
+    if lse is not None:
+        need("lse", lse, (B, Hq, S_q), (torch.float32,))
+    if flags_out is not None:
+        need("flags_out", flags_out, flags_shape(B, Hq, S_q, S_k, tile_n, sub_rows),
+             (torch.int64, torch.uint64))
+    if dbg_qk_acc is not None:
+        need("dbg_qk_acc", dbg_qk_acc, (B, Hq, S_q, S_k), (torch.int32,))
+    if v8 is not None:
+        need("v8", v8, (B, Hkv, n_kt, D, 64), codes)
+        need("v_scale", v_scale, (B, Hkv, n_kt), (torch.float32,))
     p = lamp_attn_params()
     p.struct_size = ctypes.sizeof(lamp_attn_params)
     p.mode = mode

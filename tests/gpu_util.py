@@ -1,5 +1,8 @@
 """Helpers for the GPU parity tests: run the HIP pipeline through the C ABI
 binding and build the oracle's view of the same seeded inputs."""
+import json
+import os
+
 import numpy as np
 import torch
 
@@ -12,6 +15,11 @@ LAMP_REPORT = {}
 
 
 def record_lamp(st):
+    path = os.environ.get("LAMP_REPORT_FILE")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps({"test": os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0],
+                                **{k: v for k, v in st.items()}}) + "\n")
     for k in ("n_subblocks", "n_split", "n_branches", "n_nonprimary", "flag_mismatch",
               "unresolved", "excluded_rows", "lse_bad", "n_bad"):
         LAMP_REPORT[k] = LAMP_REPORT.get(k, 0) + int(st.get(k, 0))

@@ -339,8 +339,9 @@ def test_empty_problems():
     q8 = torch.empty((1, 2, 0, 128), dtype=torch.uint8, device=dev)
     k8 = torch.empty((1, 1, 0, 128), dtype=torch.uint8, device=dev)
     s = torch.empty((1, 2, 0), dtype=torch.float32, device=dev)
+    sk = torch.empty((1, 1, 0), dtype=torch.float32, device=dev)
     m = torch.zeros((1, 2, 0, 1), dtype=torch.int64, device=dev)
-    out = lamp.lamp_attn_fwd(q, k, k, q8, k8, s, s, m, code="i8", causal=True, tile_m=128,
+    out = lamp.lamp_attn_fwd(q, k, k, q8, k8, s, sk, m, code="i8", causal=True, tile_m=128,
                              tiles_per_bit=1, words_per_row=1)
     assert out.shape == (1, 2, 0, 128)
     m2 = lamp.lamp_build_mask(0, 2, 100, 100, 128, 64, 1, 0.5, 1, device=dev)
