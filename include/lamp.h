@@ -351,6 +351,25 @@ size_t lamp_decode_workspace_bytes(int64_t B, int64_t Hkv, int64_t S_k, int64_t 
 lamp_status lamp_decode_fwd(const lamp_decode_params* p, void* workspace,
                             size_t workspace_bytes, void* stream);
 
+/*
+ * lamp_decode_fwd_noalloc -- lamp_decode_fwd without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * The split partials go to a fixed scratch array inside the library, one
+ * copy per GPU, LAMP_DECODE_SCRATCH_BYTES (32 MiB) in size, held from the
+ * first call on that GPU until the process ends (its device address is
+ * looked up on that first call).  The call allocates nothing.  Sizes whose
+ * partials (lamp_decode_workspace_bytes) exceed the scratch return
+ * LAMP_ERR_UNSUPPORTED.  Every call on one GPU shares that GPU's scratch:
+ * calls that may overlap on one GPU (different streams, or host threads)
+ * race and give undefined results; calls ordered on one stream are safe.
+ * The scratch keeps the last call's partials; nothing in it needs to start
+ * at zero.  Everything else as for lamp_decode_fwd.
+ */
+#define LAMP_DECODE_SCRATCH_BYTES (32u << 20)
+lamp_status lamp_decode_fwd_noalloc(const lamp_decode_params* p, void* stream);
+
 /* Static name of a status code. */
 const char* lamp_status_string(lamp_status s);
 

@@ -21,10 +21,37 @@
 //     writes its unnormalised partial (m, l, O) to the caller's workspace;
 //   * decode_merge_kernel: one workgroup per (b, KV head, column) combines
 //     the splits' partials (log-sum-exp merge) and writes O and LSE.
+#include <mutex>
+
 #include "attn_kernel.h"
 #include "lamp_internal.h"
 
+// Fixed scratch for the split partials of lamp_decode_fwd_noalloc: a
+// file-scope device array, one copy per GPU.  Host code never passes its
+// name to a kernel (in host code the name is not a device address); it uses
+// the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) char scratch[lamp::kDecodeScratchBytes];
+
 namespace lamp {
+
+hipError_t decode_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 namespace {
 

@@ -403,8 +403,13 @@ size_t lamp_decode_workspace_bytes(int64_t B, int64_t Hkv, int64_t S_k, int64_t 
   return (size_t)(B * Hkv * n_split * 32 * (D + 2) * (int64_t)sizeof(float));
 }
 
-lamp_status lamp_decode_fwd(const lamp_decode_params* p, void* workspace, size_t workspace_bytes,
-                            void* stream) {
+// Validates p and fills a; the partials go to `workspace` (at least
+// lamp_decode_workspace_bytes bytes, checked by the callers).  With
+// need_ws false the workspace is not checked (the fixed scratch is put in
+// place afterwards).
+static lamp_status decode_prepare(const lamp_decode_params* p, void* workspace, bool need_ws,
+                                  lamp::DecodeArgs* out_args, bool* empty) {
+  *empty = false;
   if (!p) return fail(LAMP_ERR_NULL, "params is NULL");
   if (p->struct_size != sizeof(lamp_decode_params))
     return fail(LAMP_ERR_UNSUPPORTED, "struct_size %u != %zu (ABI mismatch)", p->struct_size,
@@ -420,11 +425,15 @@ lamp_status lamp_decode_fwd(const lamp_decode_params* p, void* workspace, size_t
   if (p->tile_m < 1) return fail(LAMP_ERR_SHAPE, "tile_m must be positive");
   if (p->causal && p->S_q > p->S_k) return fail(LAMP_ERR_UNSUPPORTED, "causal needs S_q <= S_k");
   if (p->S_k > kMaxSeq) return fail(LAMP_ERR_UNSUPPORTED, "S_k above %lld", (long long)kMaxSeq);
-  if (p->B == 0 || p->Hq == 0 || p->S_q == 0) return ok();
+  if (p->B == 0 || p->Hq == 0 || p->S_q == 0) {
+    *empty = true;
+    return ok();
+  }
   if (p->S_k == 0) return fail(LAMP_ERR_SHAPE, "S_k == 0 with queries");
-  if (!p->q8 || !p->q_scale || !p->k8 || !p->k_scale || !p->v8 || !p->v_scale || !p->out || !workspace)
+  if (!p->q8 || !p->q_scale || !p->k8 || !p->k_scale || !p->v8 || !p->v_scale || !p->out ||
+      (need_ws && !workspace))
     return fail(LAMP_ERR_NULL, "q8, k8, v8, their scales, out and workspace are required");
-  if (!aligned16(p->q8) || !aligned16(p->k8) || !aligned16(p->v8) || !aligned16(workspace))
+  if (!aligned16(p->q8) || !aligned16(p->k8) || !aligned16(p->v8) || (need_ws && !aligned16(workspace)))
     return fail(LAMP_ERR_ALIGN, "codes and workspace need 16-byte alignment");
   if (((reinterpret_cast<uintptr_t>(p->out)) & 1u) ||
       ((reinterpret_cast<uintptr_t>(p->q_scale) | reinterpret_cast<uintptr_t>(p->k_scale) |
@@ -432,9 +441,6 @@ lamp_status lamp_decode_fwd(const lamp_decode_params* p, void* workspace, size_t
     return fail(LAMP_ERR_ALIGN, "out, scales and lse need their element alignment");
   for (int i = 0; i < 3; ++i)
     if (p->o_str[i] < 0) return fail(LAMP_ERR_SHAPE, "negative output stride");
-  const size_t need = lamp_decode_workspace_bytes(p->B, p->Hkv, p->S_k, p->D);
-  if (workspace_bytes < need)
-    return fail(LAMP_ERR_SHAPE, "workspace %zu bytes < %zu", workspace_bytes, need);
   lamp::DecodeArgs a{};
   a.q8 = static_cast<const uint8_t*>(p->q8);
   a.q_scale = p->q_scale;
@@ -465,9 +471,46 @@ lamp_status lamp_decode_fwd(const lamp_decode_params* p, void* workspace, size_t
   a.causal = p->causal;
   a.sm_scale = p->sm_scale > 0.f ? p->sm_scale : (float)(1.0 / std::sqrt((double)p->D));
   a.bf16 = p->out_dtype == LAMP_BF16;
+  if (workspace != nullptr) {
+    const int64_t nslot = (int64_t)a.B * a.Hkv * a.n_split * 32;
+    a.ws_o = static_cast<float*>(workspace);
+    a.ws_ml = a.ws_o + nslot * a.D;
+  }
+  *out_args = a;
+  return ok();
+}
+
+lamp_status lamp_decode_fwd_noalloc(const lamp_decode_params* p, void* stream) {
+  lamp::DecodeArgs a;
+  bool empty = false;
+  // validate first with a placeholder workspace; the partials' real home is
+  // only looked up for a call that launches
+  const lamp_status st = decode_prepare(p, nullptr, false, &a, &empty);
+  if (st != LAMP_OK || empty) return st;
+  const size_t need = lamp_decode_workspace_bytes(p->B, p->Hkv, p->S_k, p->D);
+  if (need > lamp::kDecodeScratchBytes)
+    return fail(LAMP_ERR_UNSUPPORTED,
+                "these sizes need %zu bytes of split partials; the fixed scratch holds %zu "
+                "(use lamp_decode_fwd with a workspace)",
+                need, lamp::kDecodeScratchBytes);
+  void* scratch = nullptr;
+  const hipError_t e = lamp::decode_scratch(&scratch);
+  if (e != hipSuccess) return hip_status(e, "scratch address");
   const int64_t nslot = (int64_t)a.B * a.Hkv * a.n_split * 32;
-  a.ws_o = static_cast<float*>(workspace);
+  a.ws_o = static_cast<float*>(scratch);
   a.ws_ml = a.ws_o + nslot * a.D;
+  return hip_status(lamp::launch_decode(a, static_cast<hipStream_t>(stream)), "decode launch");
+}
+
+lamp_status lamp_decode_fwd(const lamp_decode_params* p, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  lamp::DecodeArgs a;
+  bool empty = false;
+  const lamp_status st = decode_prepare(p, workspace, true, &a, &empty);
+  if (st != LAMP_OK || empty) return st;
+  const size_t need = lamp_decode_workspace_bytes(p->B, p->Hkv, p->S_k, p->D);
+  if (workspace_bytes < need)
+    return fail(LAMP_ERR_SHAPE, "workspace %zu bytes < %zu", workspace_bytes, need);
   return hip_status(lamp::launch_decode(a, static_cast<hipStream_t>(stream)), "decode launch");
 }
 

@@ -140,4 +140,10 @@ hipError_t launch_attn_d128(const AttnArgs& a, const AttnConfig& c, hipStream_t 
 hipError_t launch_attn_d256(const AttnArgs& a, const AttnConfig& c, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 
+// Size of the fixed device scratch of lamp_decode_fwd_noalloc (one copy per
+// GPU, held until the process ends), and the device address of the current
+// GPU's copy (looked up once per device, with that device current).
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+hipError_t decode_scratch(void** ptr);
+
 }  // namespace lamp

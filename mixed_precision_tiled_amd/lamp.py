@@ -372,6 +372,37 @@ def lamp_decode_fwd(q8, q_scale, k8, k_scale, v8, v_scale, *, causal, tile_m, dt
     return out
 
 
+_lib.lamp_decode_fwd_noalloc.restype = _i32
+_lib.lamp_decode_fwd_noalloc.argtypes = [ctypes.POINTER(lamp_decode_params), _vp]
+LAMP_DECODE_SCRATCH_BYTES = 32 << 20
+
+
+def lamp_decode_fwd_noalloc(q8, q_scale, k8, k_scale, v8, v_scale, *, causal, tile_m, out,
+                            sm_scale=0.0, lse=None):
+    """lamp_decode_fwd with the split partials in the library's fixed
+    per-GPU scratch: no device memory is allocated (``out`` is required)."""
+    B, Hq, S_q, D = q8.shape
+    _, Hkv, S_k, _ = k8.shape
+    if out.dtype not in _DT16 or tuple(out.shape) != (B, Hq, S_q, D):
+        raise ValueError("out must be float16/bfloat16 [B, Hq, S_q, D]")
+    for t in (q8, q_scale, k8, k_scale, v8, v_scale, lse):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("codes, scales and lse must be contiguous")
+    p = lamp_decode_params()
+    p.struct_size = ctypes.sizeof(lamp_decode_params)
+    p.causal = int(bool(causal))
+    p.sm_scale = sm_scale
+    p.out_dtype = _DT16[out.dtype]
+    p.B, p.Hq, p.Hkv, p.S_q, p.S_k, p.D = B, Hq, Hkv, S_q, S_k, D
+    p.q8, p.q_scale, p.tile_m = q8.data_ptr(), q_scale.data_ptr(), tile_m
+    p.k8, p.k_scale, p.v8, p.v_scale = k8.data_ptr(), k_scale.data_ptr(), v8.data_ptr(), v_scale.data_ptr()
+    p.out = out.data_ptr()
+    p.o_str = _strides3(out)
+    p.lse = None if lse is None else lse.data_ptr()
+    _check(_lib.lamp_decode_fwd_noalloc(ctypes.byref(p), _stream(q8)))
+    return out
+
+
 def flags_shape(B, Hq, S_q, S_k, tile_n=64, sub_rows=32):
     return (B, Hq, cdiv(S_q, sub_rows), max(1, cdiv(cdiv(S_k, tile_n), 64)))
 

@@ -121,6 +121,36 @@ def test_decode_validation(lamp):
     assert f(None, ws, need, None) == 1
 
 
+def test_decode_noalloc_validation(lamp):
+    # the entry point without a workspace validates like lamp_decode_fwd and
+    # refuses sizes whose partials exceed its fixed scratch, before it looks
+    # up the scratch or launches anything (no GPU needed here)
+    from mixed_precision_tiled_amd.lamp import lamp_decode_params as P
+    f = _lib(lamp).lamp_decode_fwd_noalloc
+
+    def params(**kw):
+        p = P()
+        p.struct_size = ctypes.sizeof(P)
+        p.causal, p.out_dtype = 1, 1
+        p.B, p.Hq, p.Hkv, p.S_q, p.S_k, p.D = 1, 8, 2, 1, 1000, 128
+        p.q8 = p.q_scale = p.k8 = p.k_scale = p.v8 = p.v_scale = p.out = 4096
+        p.tile_m = 64
+        p.o_str[:] = [8 * 128, 128, 128]
+        for key, val in kw.items():
+            setattr(p, key, val)
+        return p
+    cases = [(dict(struct_size=4), 3), (dict(D=256), 3), (dict(Hkv=3), 3), (dict(k8=None), 1),
+             (dict(q8=4100), 4), (dict(B=-1), 2), (dict(B=0), 0),
+             # 64 x 8 groups over 131072 keys: 545 MB of partials > 32 MiB
+             (dict(B=64, Hq=8, Hkv=8, S_k=131072), 3)]
+    assert lamp.lamp_decode_workspace_bytes(64, 8, 131072, 128) > lamp.LAMP_DECODE_SCRATCH_BYTES
+    assert lamp.LAMP_DECODE_SCRATCH_BYTES == 32 << 20
+    for kw, st in cases:
+        assert f(ctypes.byref(params(**kw)), None) == st, kw
+    assert "fixed scratch" in lamp.lamp_last_error()
+    assert f(None, None) == 1
+
+
 def test_library_exports_every_declared_symbol(lamp):
     names = declared_functions()
     assert set(names) >= {"lamp_quantize_blocks", "lamp_build_mask", "lamp_attn_fwd",
