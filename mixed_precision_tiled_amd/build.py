@@ -20,6 +20,13 @@ BUILD = os.path.join(HERE, "_build")
 SOURCES = ["lamp_api.cpp", "quant_mask.hip", "attn_d64.hip", "attn_d128.hip", "attn_d256.hip",
            "decode.hip"]
 
+# Per-unit flags.  Head dim 256 runs one wave per SIMD with 512 registers;
+# there the compiler would put every MFMA accumulator in AGPRs, and the
+# logits would travel AGPR -> VGPR -> AGPR between the products and the
+# softmax.  The VGPR form keeps them in VGPRs (AGPRs still take the
+# overflow).
+UNIT_FLAGS = {"attn_d256.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
+
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # packed fp32 VALU forms are switched off for every HIP translation unit
@@ -42,7 +49,7 @@ def build(verbose=False, jobs=None):
 
     def compile_one(src):
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-        _run([HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        _run([HIPCC, *FLAGS, *UNIT_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
         return obj
 
     def compile_probe():
