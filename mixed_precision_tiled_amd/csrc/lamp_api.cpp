@@ -105,6 +105,7 @@ lamp_status lamp_quantize_blocks_varlen(const void* x, int32_t x_dtype, int64_t 
   a.D = (int32_t)D;
   a.block_rows = block_rows;
   a.nb = (int32_t)nb;
+  a.chunk_shift = D == 64 ? 3 : D == 128 ? 4 : 5;    // log2(D / 8), D in {64, 128, 256}
   a.seqlens = seqlens;
   a.bf16 = x_dtype == LAMP_BF16;
   a.e4m3 = code_dtype == LAMP_E4M3;

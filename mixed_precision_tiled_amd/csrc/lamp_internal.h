@@ -15,6 +15,7 @@ struct QuantArgs {
   int64_t sb, sh, ss;          // element strides of x
   int32_t B, H, S, D;
   int32_t block_rows, nb;      // nb = ceil(S / block_rows)
+  int32_t chunk_shift;         // log2(D / 8)
   const int32_t* seqlens;      // [B] or nullptr (all S)
   bool bf16, e4m3;
 };

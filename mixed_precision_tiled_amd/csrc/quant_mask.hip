@@ -19,6 +19,20 @@ namespace {
 
 constexpr int kQuantThreads = 256;
 
+// Largest of the two 16-bit lanes, each taken as an unsigned integer.
+__device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                __builtin_bit_cast(u16x2, b)));
+}
+
+// Byte 0 of each of four words, packed low to high.
+__device__ __forceinline__ uint32_t pack_low_bytes(uint32_t b0, uint32_t b1, uint32_t b2,
+                                                   uint32_t b3) {
+  const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
+  const uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
+  return lo | (hi << 16);
+}
+
 template <bool BF16, bool E4M3, int CPT>
 __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantArgs a) {
   const int blk = blockIdx.x % a.nb;
@@ -30,8 +44,11 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantArgs a) {
   // rows at or past the sequence length are padding: not read, zero
   const int len = a.seqlens != nullptr ? min(max(ld_uniform(a.seqlens + b), 0), a.S) : a.S;
   const int rows_live = min(rows, max(len - r0, 0));
-  const int cpr = a.D / 8;                      // 8-element chunks per row
-  const int nch = rows * cpr;
+  // 8-element chunks: D / 8 per row (a power of two), chunk c = row * D / 8 +
+  // column / 8, so the live rows' chunks are exactly c < n_live
+  const int cs = a.chunk_shift;
+  const int nch = rows << cs;
+  const int n_live = rows_live << cs;
   const char* base = reinterpret_cast<const char*>(a.x) +
                      2 * (b * a.sb + h * a.sh + (int64_t)r0 * a.ss);
   const int tid = threadIdx.x;
@@ -43,30 +60,31 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantArgs a) {
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const int c = tid + i * kQuantThreads;
-    const int cl = (c < nch && c / cpr < rows_live) ? c : 0;
-    const int r = cl / cpr, col = (cl % cpr) * 8;
+    const int cl = c < n_live ? c : 0;
+    const int r = cl >> cs, col = (cl & ((1 << cs) - 1)) * 8;
     cache[i] = ld_global16(base + 2 * ((int64_t)r * a.ss + col));
   }
-  float amax = 0.f;
+  // absmax on the bit patterns: for finite fp16 / bf16 values the magnitude
+  // bits (sign cleared) order like the magnitudes themselves
+  uint32_t am2 = 0u;
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const int c = tid + i * kQuantThreads;
-    if (!(c < nch && c / cpr < rows_live)) cache[i] = u32x4{0u, 0u, 0u, 0u};
+    if (!(c < n_live)) cache[i] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      amax = fmaxf(amax, fabsf(from16<BF16>(cache[i][e] & 0xFFFFu)));
-      amax = fmaxf(amax, fabsf(from16<BF16>(cache[i][e] >> 16)));
-    }
+    for (int e = 0; e < 4; ++e) am2 = max_u16x2(am2, cache[i][e] & 0x7FFF7FFFu);
   }
+  uint32_t am = max(am2 & 0xFFFFu, am2 >> 16);
   // block absmax: wave butterfly, then across the 4 waves through LDS
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-  __shared__ float red[kQuantThreads / 64];
-  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  for (int off = 32; off >= 1; off >>= 1) am = max(am, (uint32_t)__shfl_xor((int)am, off, 64));
+  __shared__ uint32_t red[kQuantThreads / 64];
+  if ((tid & 63) == 0) red[tid >> 6] = am;
   __syncthreads();
-  amax = red[0];
+  am = red[0];
 #pragma unroll
-  for (int w = 1; w < kQuantThreads / 64; ++w) amax = fmaxf(amax, red[w]);
+  for (int w = 1; w < kQuantThreads / 64; ++w) am = max(am, red[w]);
+  const float amax = from16<BF16>(am);
 
   const float qmax = E4M3 ? 448.f : 127.f;
   const bool nz = amax > 0.f;
@@ -86,23 +104,29 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantArgs a) {
         y[2 * e + 1] = from16<BF16>(cache[i][e] >> 16) * inv;
       }
       u32x2 packed;
-      if (!nz) {
-        packed = u32x2{0u, 0u};
-      } else if constexpr (E4M3) {
+      if constexpr (E4M3) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) y[e] = fminf(fmaxf(y[e], -448.f), 448.f);
         packed.x = f32x4_to_e4m3(y[0], y[1], y[2], y[3]);
         packed.y = f32x4_to_e4m3(y[4], y[5], y[6], y[7]);
+        // an all-zero block encodes as +0 whatever the sign of its zeros
+        if (!nz) packed = u32x2{0u, 0u};
       } else {
-        uint32_t w[2] = {0u, 0u};
+        // |y| <= 127 (1 + 2^-24)^2 < 127.5, so round-half-even(y) lies in
+        // [-127, 127] with no clamp.  y + 1.5 * 2^23 is rounded once, to an
+        // integer (the constant is even, so ties go the same way as for y),
+        // and its low byte is that integer in two's complement.  The sum
+        // must not be fused with the product y = x * inv.
+        uint32_t t[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          float r = fminf(fmaxf(__builtin_rintf(y[e]), -127.f), 127.f);
-          w[e >> 2] |= ((uint32_t)(int)r & 0xFFu) << (8 * (e & 3));
+#pragma clang fp contract(off)
+          t[e] = __builtin_bit_cast(uint32_t, y[e] + 12582912.f);
         }
-        packed = u32x2{w[0], w[1]};
+        packed = u32x2{pack_low_bytes(t[0], t[1], t[2], t[3]), pack_low_bytes(t[4], t[5], t[6], t[7])};
       }
-      const int r = c / cpr, col = (c % cpr) * 8;
+      // (int8: an all-zero block has inv = 0, so every y is +-0, every code 0)
+      const int r = c >> cs, col = (c & ((1 << cs) - 1)) * 8;
       *reinterpret_cast<u32x2*>(out + (int64_t)r * a.D + col) = packed;
     }
   }
