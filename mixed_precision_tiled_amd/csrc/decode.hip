@@ -14,8 +14,10 @@
 //     sized to give the grid about one wave per SIMD); the
 //     group's queries (heads_per_group x S_q <= 32 columns) are the B operand
 //     of int8 32x32x32 MFMAs (S^T = K8 Q8^T, K8 straight from global memory
-//     into registers, each byte read once, three tiles' codes in flight
-//     while one is computed); online softmax per column; V
+//     into registers, each byte read once, the next tile's codes in flight
+//     while one is computed); online softmax per column (the key mask only
+//     on tiles that reach past a column's last key, O rescaled only when a
+//     column's maximum moves); V
 //     codes are converted to 16 bits into LDS in the prefill kernel's layout
 //     and multiplied as O^T += V^T P^T, with sV folded into P.  Each wave
 //     writes its unnormalised partial (m, l, O) to the caller's workspace;
@@ -80,6 +82,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   const float sQ = a.q_scale[((int64_t)b * a.Hq + h) * a.n_qt + i / a.tile_m];
   // largest key this column may see (-1: a padding column)
   const int key_lim = !col_live ? -1 : (a.causal ? min(i + a.S_k - a.S_q, a.S_k - 1) : a.S_k - 1);
+  // a tile needs the key mask only if it reaches past a live column's limit
+  // (padding columns are never written)
+  const int key_lim_m = col_live ? key_lim : 0x7FFFFFFF;
 
   const uint8_t* k8base = a.k8 + (int64_t)grp * a.S_k * D;
   const uint8_t* v8base = a.v8 + (int64_t)grp * a.S_k * D;
@@ -144,22 +149,31 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       acc1 = mfma_i8(kf1[t], q8[t], acc1);
     }
     const float c = c_log * sK;
-    const int lim_rel = key_lim - key0 - 4 * hf;
     float x[32];
+    if (wave_any(key0 + SH::TN - 1 > key_lim_m)) {
+      const int lim_rel = key_lim - key0 - 4 * hf;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int v0 = acc0[e], v1 = acc1[e];
-      x[e] = kofs(e) <= lim_rel ? (float)v0 * c : kNegInf;
-      x[16 + e] = kofs(16 + e) <= lim_rel ? (float)v1 * c : kNegInf;
+      for (int e = 0; e < 16; ++e) {
+        const int v0 = acc0[e], v1 = acc1[e];
+        x[e] = kofs(e) <= lim_rel ? (float)v0 * c : kNegInf;
+        x[16 + e] = kofs(16 + e) <= lim_rel ? (float)v1 * c : kNegInf;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        x[e] = (float)acc0[e] * c;
+        x[16 + e] = (float)acc1[e] * c;
+      }
     }
-    // online softmax with the exact running maximum
+    // online softmax with the exact running maximum; the rescale of O and l
+    // by alpha = exp2(m_old - m_new) is skipped when no column's maximum
+    // moved (alpha would be exactly 1)
     float mx = x[0];
 #pragma unroll
     for (int e = 1; e < 32; ++e) mx = fmaxf(mx, x[e]);
     mx = halves_max(mx);
     const float m_new = fmaxf(m_run, mx);
     const float msub = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = m_run == kNegInf ? 0.f : exp2_fast(m_run - m_new);
     float psum = 0.f;
     uint32_t pk[16];
 #pragma unroll
@@ -168,10 +182,14 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       psum += p0 + p1;
       pk[e >> 1] = pack16x2<BF16>(p0 * sV, p1 * sV);     // the V scale rides on P
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+    if (wave_any(m_new != m_run)) {
+      const float alpha = m_run == kNegInf ? 0.f : exp2_fast(m_run - m_new);
+      l_run *= alpha;
 #pragma unroll
-    for (int db = 0; db < SH::ND; ++db) O[db] *= alpha;
+      for (int db = 0; db < SH::ND; ++db) O[db] *= alpha;
+      m_run = m_new;
+    }
+    l_run += psum;
 
     // V codes -> 16-bit into LDS: row = key, logical 16-byte chunk lc at
     // position lc ^ swz(row) (the prefill kernel's V layout)
@@ -209,26 +227,20 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       }
     }
   };
-  // four register sets in a ring (unrolled by four so that each names its
-  // set statically): three tiles in flight while one is computed.  The
-  // prefetches are unconditional (past the split's last tile they reload
+  // two register sets (unrolled by two so that each names its set
+  // statically): one tile in flight while the other is computed.  A deeper
+  // ring holds more codes in flight but pushes them through AGPRs (copies
+  // on every tile), which costs more than it hides.  The prefetches are
+  // unconditional (past the split's last tile they reload
   // that tile, an L2 hit): conditional loads would make the wait for the
   // current set count every load in flight.
-  TileCodes t0, t1, t2, t3;
-  if (kt0 < kt1) {
-    load_tile(kt0, t0);
-    load_tile(min(kt0 + 1, kt1 - 1), t1);
-    load_tile(min(kt0 + 2, kt1 - 1), t2);
-  }
-  for (int kt = kt0; kt < kt1; kt += 4) {
-    load_tile(min(kt + 3, kt1 - 1), t3);
+  TileCodes t0, t1;
+  if (kt0 < kt1) load_tile(kt0, t0);
+  for (int kt = kt0; kt < kt1; kt += 2) {
+    load_tile(min(kt + 1, kt1 - 1), t1);
     compute_tile(kt, t0);
-    load_tile(min(kt + 4, kt1 - 1), t0);
+    load_tile(min(kt + 2, kt1 - 1), t0);
     if (kt + 1 < kt1) compute_tile(kt + 1, t1);
-    load_tile(min(kt + 5, kt1 - 1), t1);
-    if (kt + 2 < kt1) compute_tile(kt + 2, t2);
-    load_tile(min(kt + 6, kt1 - 1), t2);
-    if (kt + 3 < kt1) compute_tile(kt + 3, t3);
   }
 
   // partial of this split: O^T block db holds rows d = 32 db + 8 (r / 4) +
