@@ -124,6 +124,10 @@ void attn_fwd_kernel(const AttnArgs a) {
   // sk0 / sk1), so that a flagged sub-block recomputes its logits from LDS
   __shared__ __attribute__((aligned(1024))) char sq0[ADAPTIVE ? SH::K8_BYTES : 16];
   __shared__ __attribute__((aligned(1024))) char sq1[ADAPTIVE ? SH::K8_BYTES : 16];
+  // 8-bit exponentials: E4M3(exp(value(c))) for every e4m3 code c (not at
+  // D = 256 in adaptive mode, whose tiles fill the LDS)
+  constexpr bool EXP8_TAB = EXP8 && !(ADAPTIVE && D >= 256);
+  __shared__ uint8_t exp8_tab[EXP8_TAB ? 256 : 4];
 
   // ---- workgroup -> (b, h, qt): XCD-contiguous chunks of the logical order
   //      (kv-head group, b) major, query tile descending, head minor.  The
@@ -148,6 +152,15 @@ void attn_fwd_kernel(const AttnArgs a) {
   if (qt * SH::TM >= Lq) return;
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  if constexpr (EXP8_TAB) {
+    // the table entries are computed exactly as the weights would be: the
+    // code's value, exp through exp2, rounded to e4m3 (visible to all waves
+    // after the barrier ahead of the main loop)
+    for (int c = tid; c < 256; c += SH::NT) {
+      const f32x2 v = e4m3x2_to_f32<false>((uint32_t)c);
+      exp8_tab[c] = (uint8_t)(f32x4_to_e4m3(exp2_fast(v.x * kLog2e), 0.f, 0.f, 0.f) & 0xFFu);
+    }
+  }
   // the wave index as a scalar, for the LDS destinations of the tile copies
   // (M0), so that they need no per-copy lane read
   const int wu = __builtin_amdgcn_readfirstlane(w);
@@ -598,6 +611,21 @@ void attn_fwd_kernel(const AttnArgs a) {
       }
       return ps0 + ps1;
     };
+    // LAZY, no branch: the weights against mref through the folded offset;
+    // `exact` is false on a lane whose folded reference m + xoff * cm was
+    // rounded (then these weights are not used: the caller weights again)
+    auto weights_folded = [&](float mref, bool& exact) -> float {
+      const float mr = (mref == kNegInf) ? 0.f : mref;
+      const float t = xo * cm;
+      const float msub = mr + t;
+      const float bb = msub - mr;
+      exact = ((mr - (msub - bb)) + (t - bb)) == 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        pk[i] = pack16x2<BF16>(exp2_fast(__builtin_fmaf(x[2 * i], cm, -msub)),
+                               exp2_fast(__builtin_fmaf(x[2 * i + 1], cm, -msub)));
+      return psum(pk);
+    };
     // the weights go to pk (LAZY keeps x; otherwise the fp32 weights
     // overwrite x in place); returns their sum
     auto weights = [&](float mref) -> float {
@@ -641,9 +669,16 @@ void attn_fwd_kernel(const AttnArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) xs[j] = fmaxf(__builtin_fmaf(x[e + j], cm, -msub), -448.f);
             const uint32_t xc = f32x4_to_e4m3(xs[0], xs[1], xs[2], xs[3]);
-            const f32x2 xlo = e4m3x2_to_f32<false>(xc), xhi = e4m3x2_to_f32<true>(xc);
-            const uint32_t pc = f32x4_to_e4m3(exp2_fast(xlo.x * kLog2e), exp2_fast(xlo.y * kLog2e),
-                                              exp2_fast(xhi.x * kLog2e), exp2_fast(xhi.y * kLog2e));
+            uint32_t pc;
+            if constexpr (EXP8_TAB) {
+              pc = (uint32_t)exp8_tab[xc & 0xFFu] | ((uint32_t)exp8_tab[(xc >> 8) & 0xFFu] << 8) |
+                   ((uint32_t)exp8_tab[(xc >> 16) & 0xFFu] << 16) |
+                   ((uint32_t)exp8_tab[xc >> 24] << 24);
+            } else {
+              const f32x2 xlo = e4m3x2_to_f32<false>(xc), xhi = e4m3x2_to_f32<true>(xc);
+              pc = f32x4_to_e4m3(exp2_fast(xlo.x * kLog2e), exp2_fast(xlo.y * kLog2e),
+                                 exp2_fast(xhi.x * kLog2e), exp2_fast(xhi.y * kLog2e));
+            }
             const uint32_t lo16 = e4m3x2_to_16<BF16, false>(pc), hi16 = e4m3x2_to_16<BF16, true>(pc);
             if constexpr (PV8) {
               pk[e >> 2] = pc;
@@ -684,10 +719,14 @@ void attn_fwd_kernel(const AttnArgs a) {
       // moves the reference and the tile is weighted again.  The rescale
       // applies to everything accumulated so far, P V of the previous tile
       // included.
-      float l_add = weights(m_run);
+      // The folded reference has no branch, so the weights share one block
+      // with the P V products and are interleaved with them; a lane whose
+      // folded reference was rounded sends the wave to the rare branch too.
+      bool exact;
+      float l_add = weights_folded(m_run, exact);
       asm volatile("" : "+v"(l_add));
       interleave_pv_softmax();
-      if (wave_any((l_add > 65536.f) | (m_run == kNegInf))) {
+      if (wave_any((l_add > 65536.f) | (m_run == kNegInf) | !exact)) {
         __builtin_amdgcn_sched_barrier(0);
         const float m_new = ceilf(fmaxf(m_run, row_max()));
         l_add = weights(m_new);
