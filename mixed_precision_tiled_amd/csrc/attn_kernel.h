@@ -158,7 +158,10 @@ void attn_fwd_kernel(const AttnArgs a) {
     // after the barrier ahead of the main loop)
     for (int c = tid; c < 256; c += SH::NT) {
       const f32x2 v = e4m3x2_to_f32<false>((uint32_t)c);
-      exp8_tab[c] = (uint8_t)(f32x4_to_e4m3(exp2_fast(v.x * kLog2e), 0.f, 0.f, 0.f) & 0xFFu);
+      // code 0xFF (what the conversion gives a logit below -464, -inf or NaN)
+      // weighs 0, as the clamped value -448 would: the weights need no clamp
+      exp8_tab[c] = c == 0xFF ? 0
+                              : (uint8_t)(f32x4_to_e4m3(exp2_fast(v.x * kLog2e), 0.f, 0.f, 0.f) & 0xFFu);
     }
   }
   // the wave index as a scalar, for the LDS destinations of the tile copies
@@ -667,7 +670,12 @@ void attn_fwd_kernel(const AttnArgs a) {
           for (int e = 0; e < 32; e += 4) {
             float xs[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) xs[j] = fmaxf(__builtin_fmaf(x[e + j], cm, -msub), -448.f);
+            for (int j = 0; j < 4; ++j) {
+              // (the table maps what the conversion makes of values below
+              // -448 to a zero weight; without it, clamp at -448)
+              xs[j] = __builtin_fmaf(x[e + j], cm, -msub);
+              if constexpr (!EXP8_TAB) xs[j] = fmaxf(xs[j], -448.f);
+            }
             const uint32_t xc = f32x4_to_e4m3(xs[0], xs[1], xs[2], xs[3]);
             uint32_t pc;
             if constexpr (EXP8_TAB) {
