@@ -187,15 +187,9 @@ void attn_fwd_kernel(const AttnArgs a) {
   // ---- Q fragments (B operand of S^T = K Q^T), resident for the whole loop
   const char* qp = reinterpret_cast<const char*>(a.q) +
                    2 * (b * a.q_sb + h * a.q_sh + (int64_t)q_row * a.q_ss);
-  // At D = 256 the 16-bit Q fragments (64 registers) are not held: the
-  // 16-bit products re-read them (the wave's own Q rows, from L2) and the
-  // registers go to the rest of the working set.
-  constexpr bool Q16_REREAD = D >= 256;
-  u32x4 q16[Q16_REREAD ? 1 : SH::NQ16];
-  if constexpr (!Q16_REREAD) {
+  u32x4 q16[SH::NQ16];
 #pragma unroll
-    for (int t = 0; t < SH::NQ16; ++t) q16[t] = ld_global16(qp + 2 * (16 * t + 8 * hf));
-  }
+  for (int t = 0; t < SH::NQ16; ++t) q16[t] = ld_global16(qp + 2 * (16 * t + 8 * hf));
   const uint8_t* q8p = a.q8 + (((int64_t)b * a.Hq + h) * a.S_q + q_row) * D;
   u32x4 q8[SH::NQ8];
   if constexpr (E4M3) {
@@ -379,11 +373,6 @@ void attn_fwd_kernel(const AttnArgs a) {
 
   auto qk16_lds = [&](const char* kb, float* x) {
     u32x4 kf0[SH::NQ16], kf1[SH::NQ16];
-    u32x4 qf[Q16_REREAD ? SH::NQ16 : 1];
-    if constexpr (Q16_REREAD) {
-#pragma unroll
-      for (int t = 0; t < SH::NQ16; ++t) qf[t] = ld_global16(qp + 2 * (16 * t + 8 * hf));
-    }
 #pragma unroll
     for (int t = 0; t < SH::NQ16; ++t) kf0[t] = ld_lds16(kb + a16[t]);
 #pragma unroll
@@ -391,9 +380,8 @@ void attn_fwd_kernel(const AttnArgs a) {
     f32x16 acc0 = f32x16{}, acc1 = f32x16{};
 #pragma unroll
     for (int t = 0; t < SH::NQ16; ++t) {
-      const u32x4 qt = Q16_REREAD ? qf[t] : q16[t];
-      acc0 = mfma16<BF16>(kf0[t], qt, acc0);
-      acc1 = mfma16<BF16>(kf1[t], qt, acc1);
+      acc0 = mfma16<BF16>(kf0[t], q16[t], acc0);
+      acc1 = mfma16<BF16>(kf1[t], q16[t], acc1);
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
