@@ -24,8 +24,11 @@ SOURCES = ["lamp_api.cpp", "quant_mask.hip", "attn_d64.hip", "attn_d128.hip", "a
 # there the compiler would put every MFMA accumulator in AGPRs, and the
 # logits would travel AGPR -> VGPR -> AGPR between the products and the
 # softmax.  The VGPR form keeps them in VGPRs (AGPRs still take the
-# overflow).
-UNIT_FLAGS = {"attn_d256.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
+# overflow).  With a single wave per SIMD nothing hides the latency of one
+# instruction behind another wave's: the ILP-oriented machine scheduler
+# spreads dependent instructions further apart.
+UNIT_FLAGS = {"attn_d256.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true",
+                                "-mllvm", "--amdgpu-sched-strategy=iterative-ilp"]}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
