@@ -90,7 +90,7 @@ struct AttnArgs {
 // Decode over an int8 key/value cache: 64-key tiles per split of the keys.
 // The split length aims at one wave per SIMD over the whole grid (1024
 // SIMDs), within [8, 32] tiles: long enough for the ring of register sets in
-// each wave (three tiles of loads in flight) to pay off, short enough to fill
+// each wave (the next tile's loads in flight) to pay off, short enough to fill
 // the chip at small batch.
 constexpr int kDecodeMinTilesPerSplit = 8;
 constexpr int kDecodeMaxTilesPerSplit = 32;
