@@ -370,6 +370,20 @@ lamp_status lamp_decode_fwd(const lamp_decode_params* p, void* workspace,
 #define LAMP_DECODE_SCRATCH_BYTES (32u << 20)
 lamp_status lamp_decode_fwd_noalloc(const lamp_decode_params* p, void* stream);
 
+/*
+ * lamp_exp8_table -- the attention kernel's 8-bit exponential of every e4m3
+ * code ("LampAttention: Look-Ahead Mixed-Precision FlashAttention for
+ * Dedicated Accelerators", Abstract: exponentials evaluated in 8-bit
+ * formats).  table: device pointer to 256 bytes; table[c] =
+ * E4M3(exp(value(c))) as the kernel computes it (value decoded by the
+ * hardware conversion, exp through exp2, rounded to e4m3), except
+ * table[0xFF] = 0: 0xFF is the code the fp32 -> e4m3 conversion gives a
+ * weight's logit below -464, -inf or NaN, and such a logit weighs 0 as one
+ * clamped to -448 would.  With 8-bit exponentials the kernel's weight of a
+ * logit x <= 0 is table[E4M3(x)].  Asynchronous on `stream`.
+ */
+lamp_status lamp_exp8_table(uint8_t* table, void* stream);
+
 /* Static name of a status code. */
 const char* lamp_status_string(lamp_status s);
 

@@ -10,6 +10,6 @@ from .lamp import (  # noqa: F401
     lamp_abi_version, lamp_attn_fwd, lamp_build_mask, lamp_build_mask_per_head,
     lamp_build_mask_template, lamp_last_error,
     lamp_quantize_blocks, lamp_quantize_v_tiles, lamp_decode_fwd, lamp_decode_workspace_bytes,
-    lamp_decode_fwd_noalloc, LAMP_DECODE_SCRATCH_BYTES,
+    lamp_decode_fwd_noalloc, LAMP_DECODE_SCRATCH_BYTES, lamp_exp8_table,
     lamp_status_string, library_path, exported_symbols,
 )

@@ -153,16 +153,8 @@ void attn_fwd_kernel(const AttnArgs a) {
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   if constexpr (EXP8_TAB) {
-    // the table entries are computed exactly as the weights would be: the
-    // code's value, exp through exp2, rounded to e4m3 (visible to all waves
-    // after the barrier ahead of the main loop)
-    for (int c = tid; c < 256; c += SH::NT) {
-      const f32x2 v = e4m3x2_to_f32<false>((uint32_t)c);
-      // code 0xFF (what the conversion gives a logit below -464, -inf or NaN)
-      // weighs 0, as the clamped value -448 would: the weights need no clamp
-      exp8_tab[c] = c == 0xFF ? 0
-                              : (uint8_t)(f32x4_to_e4m3(exp2_fast(v.x * kLog2e), 0.f, 0.f, 0.f) & 0xFFu);
-    }
+    // (visible to all waves after the barrier ahead of the main loop)
+    for (int c = tid; c < 256; c += SH::NT) exp8_tab[c] = (uint8_t)exp8_code((uint32_t)c);
   }
   // the wave index as a scalar, for the LDS destinations of the tile copies
   // (M0), so that they need no per-copy lane read

@@ -112,6 +112,11 @@ lamp_status lamp_quantize_blocks_varlen(const void* x, int32_t x_dtype, int64_t 
   return hip_status(lamp::launch_quantize(a, static_cast<hipStream_t>(stream)), "quantize launch");
 }
 
+lamp_status lamp_exp8_table(uint8_t* table, void* stream) {
+  if (!table) return fail(LAMP_ERR_NULL, "table is required");
+  return hip_status(lamp::launch_exp8_table(table, static_cast<hipStream_t>(stream)), "exp8 table launch");
+}
+
 lamp_status lamp_quantize_v_tiles(const void* v, int32_t v_dtype, int64_t B, int64_t H, int64_t S,
                                   int64_t D, int64_t sb, int64_t sh, int64_t ss,
                                   const int32_t* seqlens, void* codes, float* scales,

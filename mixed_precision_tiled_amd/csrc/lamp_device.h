@@ -222,4 +222,17 @@ __device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t vof
 
 __device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0ull; }
 
+// 8-bit exponential of one e4m3 code c (LampAttention, Abstract: exponentials
+// in 8-bit formats): E4M3(exp(value(c))), the value decoded by the hardware
+// conversion, exp taken through exp2, the result rounded to e4m3.  Code 0xFF,
+// which the fp32 -> e4m3 conversion gives logits below -464, -inf and NaN,
+// weighs 0, as a logit clamped to -448 would (its exponential is below half
+// the smallest e4m3 subnormal).
+__device__ __forceinline__ uint32_t exp8_code(uint32_t c) {
+  if (c == 0xFFu) return 0u;
+  const f32x2 v = __builtin_amdgcn_cvt_pk_f32_fp8((int)c, false);
+  const int r = __builtin_amdgcn_cvt_pk_fp8_f32(exp2_fast(v.x * kLog2e), 0.f, 0, false);
+  return (uint32_t)r & 0xFFu;
+}
+
 }  // namespace lamp

@@ -134,6 +134,7 @@ struct AttnConfig {
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
 hipError_t launch_quantize_v(const VQuantArgs& a, hipStream_t s);
+hipError_t launch_exp8_table(uint8_t* out, hipStream_t s);
 hipError_t launch_build_mask(const MaskArgs& a, hipStream_t s);
 hipError_t launch_build_mask_template(const TemplateMaskArgs& a, hipStream_t s);
 hipError_t launch_attn_d64(const AttnArgs& a, const AttnConfig& c, hipStream_t s);

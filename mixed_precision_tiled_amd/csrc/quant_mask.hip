@@ -309,6 +309,16 @@ hipError_t launch_quantize_v(const VQuantArgs& a, hipStream_t s) {
   return a.bf16 ? launch_quant_v_t<true>(a, s) : launch_quant_v_t<false>(a, s);
 }
 
+// The attention kernel's 8-bit exponential table, one thread per code.
+__global__ __launch_bounds__(256) void exp8_table_kernel(uint8_t* out) {
+  out[threadIdx.x] = (uint8_t)exp8_code(threadIdx.x);
+}
+
+hipError_t launch_exp8_table(uint8_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(exp8_table_kernel, dim3(1), dim3(256), 0, s, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_build_mask(const MaskArgs& a, hipStream_t s) {
   const unsigned blocks = (unsigned)((a.total_words + kMaskWordsPerBlock - 1) / kMaskWordsPerBlock);
   hipLaunchKernelGGL(build_mask_kernel, dim3(blocks), dim3(64 * kMaskWordsPerBlock), 0, s, a);

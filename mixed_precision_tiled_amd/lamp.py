@@ -76,6 +76,8 @@ _lib.lamp_build_mask_template.restype = _i32
 _lib.lamp_build_mask_template.argtypes = [_i64, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _i32,
                                           _i32, _vp, _i32, _vp]
 _lib.lamp_attn_fwd.argtypes = [ctypes.POINTER(lamp_attn_params), _vp]
+_lib.lamp_exp8_table.restype = _i32
+_lib.lamp_exp8_table.argtypes = [_vp, _vp]
 _lib.lamp_status_string.restype = ctypes.c_char_p
 _lib.lamp_status_string.argtypes = [_i32]
 _lib.lamp_last_error.restype = ctypes.c_char_p
@@ -235,6 +237,14 @@ def lamp_build_mask_template(B, Hq, S_q, S_k, tile_m, tile_n, tiles_per_bit, sin
                                          sink_groups, band_groups, stride_groups, _ptr(mask), W,
                                          _stream(mask)))
     return mask
+
+
+def lamp_exp8_table(device="cuda"):
+    """The attention kernel's 8-bit exponential of every e4m3 code: uint8
+    tensor [256] on `device` (entry 0xFF is 0)."""
+    table = torch.empty((256,), dtype=torch.uint8, device=device)
+    _check(_lib.lamp_exp8_table(_ptr(table), _stream(table)))
+    return table
 
 
 def lamp_attn_fwd(q, k, v, q8, k8, q_scale, k_scale, mask, *, code, causal, tile_m,

@@ -408,3 +408,10 @@ def test_mfma_probe_library_loads():
     assert f(2, 1, 1, 0, 16, 16, None) == -1     # unknown kind
     assert f(0, 0, 1, 0, 16, 16, None) == -1     # no workgroups
     assert f(0, 1, 1, 0, None, 16, None) == -1   # no sink
+
+
+def test_exp8_table_validation(lamp):
+    # a null table is refused before anything reaches the GPU
+    f = _lib(lamp).lamp_exp8_table
+    assert f(None, None) == 1
+    assert "table" in lamp.lamp_last_error()

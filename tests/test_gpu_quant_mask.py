@@ -241,3 +241,19 @@ def test_quant_v_tiles_rounding_midpoints():
     v[0, 0, 0, 0] = 448.0
     print("[quant v] midpoints", flush=True)
     assert_v_tiles_equal(v)
+
+
+def test_exp8_table_exhaustive():
+    """The attention kernel's 8-bit exponential table against the oracle's
+    E4M3(exp(value)) on all 128 codes of non-positive logits (+0 and
+    0x80..0xFE); 0xFF, the conversion's code for logits below -464, -inf and
+    NaN, must weigh what a logit clamped to -448 weighs (0)."""
+    from oracle import attention as oa
+    t = L().lamp_exp8_table(device=dev()).cpu().numpy()
+    codes = np.array([0x00] + list(range(0x80, 0xFF)), np.uint8)
+    got = oe.decode(t[codes])
+    want = oa.exp8_of_code(codes)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(hex(codes[i]), got[i], want[i]) for i in bad[:8]]
+    assert t[0xFF] == 0 and oa.exp8(np.array([-1000.0, -np.inf]))[0] == 0.0
+    assert int((got > 0).sum()) == 79
