@@ -2,8 +2,10 @@
 
 |O_gpu - O_ref| <= max(atol, ulp_dtype(O_ref)) + extra, element by element,
 where atol is 2e-3 for fp16 outputs and 1e-2 for bf16 outputs, and extra is
-the widening for possible 8-bit rounding flips on the LampAttention paths
-(zero on the TileMix path).  One unit in the last place of the output dtype
+the widening on the LampAttention paths for what the weights may move by
+within the logit error bounds (e4m3 rounding flips, e4m3 weights at a
+running maximum that may be off, fp32 weights' exponent errors; zero on the
+TileMix path).  One unit in the last place of the output dtype
 covers the final rounding of O itself when |O| is large enough that half an
 ulp exceeds atol (bf16: |O| >= 2).
 
@@ -61,7 +63,7 @@ def check_lamp(res, O_gpu, dtype, flags_gpu=None, lse_gpu=None, keep=None):
     own flags of the sub-block pick the branch with the same flags (none
     matching is a flag mismatch); without GPU flags any branch may match.  The
     rows of the sub-block must then lie within the tolerance (widened by the
-    branch's bound for e4m3 rounding flips) of that branch's O, and the LSE
+    branch's bound on what its weights may move by) of that branch's O, and the LSE
     within the branch's LSE bound.  O_gpu, lse_gpu: rows in the order of the
     oracle's rows; flags_gpu: [n_sb, n_kt] bool in the order of its
     sub-blocks; keep: [R] bool, rows to compare (padding rows of a

@@ -40,7 +40,7 @@ def pytest_terminal_summary(terminalreporter, exitstatus, config):
         terminalreporter.write_line(
             "lamp acceptance: sub-blocks {} | decisions within the error bound (both ways) {} | "
             "non-primary branches picked {} | flag mismatches {} | branch-cap overflows {} | "
-            "rows excluded {} | max e4m3-flip widening {:.2e} | max |O - oracle| {:.2e}".format(
+            "rows excluded {} | max widening {:.2e} | max |O - oracle| {:.2e}".format(
                 r.get("n_subblocks", 0), r.get("n_split", 0), r.get("n_nonprimary", 0),
                 r.get("flag_mismatch", 0), r.get("unresolved", 0), r.get("excluded_rows", 0),
                 r.get("max_extra", 0.0), r.get("max_err", 0.0)))

@@ -211,6 +211,32 @@ LAMP = [
 ]
 
 
+def test_exp8_extreme_logit_spread():
+    """8-bit exponentials on mask routing where logits lie more than 464 below
+    the row maximum: a sink key (Q and K share a large channel) dominates every
+    row by about 500.  The oracle clamps such a difference to -448, whose
+    weight is 0; the kernel's conversion gives code 0xFF there, which its table
+    maps to 0 without a clamp.  The sink's own weight is exactly 1 on both
+    sides and the output is the sink's V row, so the widening is zero."""
+    cfg = small_cfg(64, 128, "bf16", "e4m3", True, 1, 2, 1, 256, 1, 0.3, exp8=True)
+    q, k, v = inputs_qk(cfg, 256, 256)
+    q, k = q.clone(), k.clone()
+    q[..., 0] = 10.0
+    k[:, :, 0, 0] = 400.0
+    print("[attn] exp8 extreme spread", flush=True)
+    g = gpu_run(cfg, q, k, v)
+    P = oracle_problem(cfg, q, k, v)
+    check_codes_and_mask(cfg, P, g)
+    rows, cols = np.arange(P.S_q), np.arange(P.S_k)
+    for h in range(cfg.Hq):
+        s8 = A.logits8(P, 0, h, rows, cols)
+        s8 = np.where(cols[None, :] <= rows[:, None] + (P.S_k - P.S_q), s8, -np.inf)
+        assert ((s8 - s8.max(axis=1, keepdims=True)) < -464).sum() > 1000
+        res, _, _ = A.attn_lamp(P, 0, h, np.arange(-(-P.S_q // P.sub_rows)), dtype=cfg.dtype)
+        assert res.extra_tol.max() < compare.ATOL[cfg.dtype]
+        check_head(cfg, P, g, 0, h)
+
+
 @pytest.mark.parametrize("case", LAMP, ids=lambda c: "d{}_m{}_{}_{}_x8{}_ad{}_s{}".format(
     c[0], c[1], c[2], c[3], int(c[12]), int(c[13]), c[8]))
 def test_small_lamp(case):
