@@ -826,8 +826,15 @@ void attn_fwd_kernel(const AttnArgs a) {
         if (!p8) pv_part(vprev, pk);
         softmax_part(x, lg, pk, False_{});
       } else {
+        // a wave in this block (P V products spread over the softmax
+        // arithmetic) takes issue priority over the other wave on its SIMD
+        // (which runs its own steps, usually for the other workgroup on the
+        // CU) while that one computes its logits: the matrix pipe is fed
+        // and the other wave's instructions fill the gaps
+        __builtin_amdgcn_s_setprio(1);
         pv_part(vprev, pk);
         softmax_part(x, lg, pk, True_{});
+        __builtin_amdgcn_s_setprio(0);
       }
     } else if (!FIRST && kt - 1 < kt_end_w) {
       pv_tile(vprev, is8_prev, svc_prev);

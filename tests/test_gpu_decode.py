@@ -68,6 +68,60 @@ def test_decode_parity(case):
             assert np.abs(glse[b, h] - lse_ref).max() <= 2e-3 + 1e-5 * np.abs(lse_ref).max()
 
 
+def test_decode_graph_replay_matches_eager():
+    # a decode step captured in a HIP graph (split and merge kernels, no
+    # memset nodes) and replayed: every replay equals the eager call bit for
+    # bit, also after new query codes are written into the captured buffer
+    m = L()
+    B, Hq, Hkv, S_k, D = 2, 32, 8, 5000, 128
+    print("[decode] graph replay", flush=True)
+    q = rand16((B, Hq, 1, D), 11, torch.bfloat16).to(dev())
+    k = rand16((B, Hkv, S_k, D), 12, torch.bfloat16).to(dev())
+    v = rand16((B, Hkv, S_k, D), 13, torch.bfloat16).to(dev())
+    q8, sq = m.lamp_quantize_blocks(q, 64, "i8")
+    k8, sk = m.lamp_quantize_blocks(k, 64, "i8")
+    v8, sv = m.lamp_quantize_blocks(v, 64, "i8")
+    out = torch.empty((B, Hq, 1, D), dtype=torch.bfloat16, device=dev())
+    ws = torch.empty(m.lamp_decode_workspace_bytes(B, Hkv, S_k, D), dtype=torch.uint8,
+                     device=dev())
+
+    def run():
+        m.lamp_decode_fwd(q8, sq, k8, sk, v8, sv, causal=True, tile_m=64, dtype=torch.bfloat16,
+                          out=out, workspace=ws)
+
+    run()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(g):
+        run()
+    for _ in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+    q2 = rand16((B, Hq, 1, D), 14, torch.bfloat16).to(dev())
+    q8b, sqb = m.lamp_quantize_blocks(q2, 64, "i8")
+    q8.copy_(q8b)
+    sq.copy_(sqb)
+    run()
+    torch.cuda.synchronize()
+    ref2 = out.clone()
+    assert not torch.equal(ref2, ref)
+    for _ in range(2):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref2)
+
+
 def test_decode_workspace_and_errors():
     m = L()
     # 79 tiles x 16 (b, KV head) groups -> 8-tile splits (the minimum), 10 of them
