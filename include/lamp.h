@@ -344,8 +344,9 @@ typedef struct {
   float* lse;               /* optional                                      */
 } lamp_decode_params;
 
-/* Workspace bytes lamp_decode_fwd needs for these sizes (0 if a size is
- * negative). */
+/* Workspace bytes lamp_decode_fwd needs for these sizes: 0 if a size is
+ * negative, SIZE_MAX for sizes no call accepts (S_k above 2^20, D above 256,
+ * or B * Hkv above 2^31 - 1). */
 size_t lamp_decode_workspace_bytes(int64_t B, int64_t Hkv, int64_t S_k, int64_t D);
 
 lamp_status lamp_decode_fwd(const lamp_decode_params* p, void* workspace,

@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 
 #include "../../include/lamp.h"
 #include "lamp_internal.h"
@@ -37,6 +38,19 @@ bool supported_d(int64_t d) { return d == 64 || d == 128 || d == 256; }
 
 constexpr int64_t kMaxSeq = 1 << 20;   // keeps every in-kernel row index in int32
 constexpr int64_t kMaxGrid = (1ll << 31) - 1;
+
+// Whether the product of the (non-negative) factors exceeds lim, without
+// forming a product that could overflow int64.
+bool product_exceeds(std::initializer_list<int64_t> factors, int64_t lim) {
+  for (int64_t f : factors)
+    if (f == 0) return false;
+  int64_t prod = 1;
+  for (int64_t f : factors) {
+    if (prod > lim / f) return true;
+    prod *= f;
+  }
+  return prod > lim;
+}
 
 lamp_status hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(LAMP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -91,7 +105,7 @@ lamp_status lamp_quantize_blocks_varlen(const void* x, int32_t x_dtype, int64_t 
     return fail(LAMP_ERR_ALIGN, "x, codes need 16-byte alignment and strides a multiple of 8");
   if (reinterpret_cast<uintptr_t>(seqlens) & 3u) return fail(LAMP_ERR_ALIGN, "seqlens needs 4-byte alignment");
   const int64_t nb = cdiv(S, block_rows);
-  if (B * H * nb > kMaxGrid) return fail(LAMP_ERR_UNSUPPORTED, "too many blocks");
+  if (product_exceeds({B, H, nb}, kMaxGrid)) return fail(LAMP_ERR_UNSUPPORTED, "too many blocks");
   lamp::QuantArgs a{};
   a.x = x;
   a.codes = codes;
@@ -133,7 +147,7 @@ lamp_status lamp_quantize_v_tiles(const void* v, int32_t v_dtype, int64_t B, int
     return fail(LAMP_ERR_ALIGN, "v, codes need 16-byte alignment and strides a multiple of 8");
   if (reinterpret_cast<uintptr_t>(seqlens) & 3u) return fail(LAMP_ERR_ALIGN, "seqlens needs 4-byte alignment");
   const int64_t n_kt = cdiv(S, 64);
-  if (B * H * n_kt > kMaxGrid) return fail(LAMP_ERR_UNSUPPORTED, "too many tiles");
+  if (product_exceeds({B, H, n_kt}, kMaxGrid)) return fail(LAMP_ERR_UNSUPPORTED, "too many tiles");
   lamp::VQuantArgs a{};
   a.v = v;
   a.codes = static_cast<uint8_t*>(codes);
@@ -184,11 +198,11 @@ lamp_status build_mask_common(int64_t B, int64_t Hq, int64_t S_q, int64_t S_k, i
   if (B == 0 || Hq == 0 || S_q == 0) return ok();
   if (!mask) return fail(LAMP_ERR_NULL, "mask is required");
   if (reinterpret_cast<uintptr_t>(mask) & 7u) return fail(LAMP_ERR_ALIGN, "mask needs 8-byte alignment");
+  if (product_exceeds({B, Hq, n_qt, words_per_row}, kMaxGrid * lamp::kMaskWordsPerBlock))
+    return fail(LAMP_ERR_UNSUPPORTED, "mask too large");
   lamp::MaskArgs a{};
   a.mask = mask;
   a.total_words = B * Hq * n_qt * words_per_row;
-  if (cdiv(a.total_words, lamp::kMaskWordsPerBlock) > kMaxGrid)
-    return fail(LAMP_ERR_UNSUPPORTED, "mask too large");
   a.seed = seed;
   a.threshold = frac_per_head ? 0 : frac_threshold(frac_16bit);
   a.words_per_row = words_per_row;
@@ -243,10 +257,11 @@ lamp_status lamp_build_mask_template(int64_t B, int64_t Hq, int64_t S_q, int64_t
   if (B == 0 || Hq == 0 || S_q == 0) return ok();
   if (!mask) return fail(LAMP_ERR_NULL, "mask is required");
   if (reinterpret_cast<uintptr_t>(mask) & 7u) return fail(LAMP_ERR_ALIGN, "mask needs 8-byte alignment");
+  if (product_exceeds({B, Hq, n_qt, words_per_row}, kMaxGrid * 256))
+    return fail(LAMP_ERR_UNSUPPORTED, "mask too large");
   lamp::TemplateMaskArgs a{};
   a.mask = mask;
   a.total_words = B * Hq * n_qt * words_per_row;
-  if (cdiv(a.total_words, 256) > kMaxGrid) return fail(LAMP_ERR_UNSUPPORTED, "mask too large");
   a.words_per_row = words_per_row;
   a.n_g = (int32_t)n_g;
   a.n_qt = (int32_t)n_qt;
@@ -326,9 +341,10 @@ lamp_status lamp_attn_fwd(const lamp_attn_params* p, void* stream) {
     if (!aligned16(p->v8)) return fail(LAMP_ERR_ALIGN, "v8 needs 16-byte alignment");
     if (reinterpret_cast<uintptr_t>(p->v_scale) & 3u) return fail(LAMP_ERR_ALIGN, "v_scale alignment");
   }
-  if (p->B * p->Hq * n_qt > kMaxGrid) return fail(LAMP_ERR_UNSUPPORTED, "grid too large");
+  if (product_exceeds({p->B, p->Hq, n_qt}, kMaxGrid)) return fail(LAMP_ERR_UNSUPPORTED, "grid too large");
   // K and V rows of one head are addressed with 32-bit byte offsets
-  if (2 * p->S_k * p->k_str[2] >= (int64_t(1) << 31) || 2 * p->S_k * p->v_str[2] >= (int64_t(1) << 31))
+  if (product_exceeds({2, p->S_k, p->k_str[2]}, kMaxGrid) ||
+      product_exceeds({2, p->S_k, p->v_str[2]}, kMaxGrid))
     return fail(LAMP_ERR_UNSUPPORTED, "K/V rows of one head span 2 GiB or more");
 
   lamp::AttnArgs a{};
@@ -404,6 +420,8 @@ extern "C" {
 
 size_t lamp_decode_workspace_bytes(int64_t B, int64_t Hkv, int64_t S_k, int64_t D) {
   if (B < 0 || Hkv < 0 || S_k < 0 || D < 0) return 0;
+  // sizes no launch accepts: a byte count no workspace can meet
+  if (S_k > kMaxSeq || D > 256 || product_exceeds({B, Hkv}, kMaxGrid)) return SIZE_MAX;
   const int64_t n_kt = cdiv(S_k, 64);
   const int64_t n_split = cdiv(n_kt, lamp::decode_tiles_per_split(B, Hkv, n_kt));
   return (size_t)(B * Hkv * n_split * 32 * (D + 2) * (int64_t)sizeof(float));
@@ -426,8 +444,8 @@ static lamp_status decode_prepare(const lamp_decode_params* p, void* workspace, 
   if (p->D != 64 && p->D != 128) return fail(LAMP_ERR_UNSUPPORTED, "decode supports D in {64,128}");
   if (!is16(p->out_dtype)) return fail(LAMP_ERR_UNSUPPORTED, "out_dtype must be LAMP_F16 or LAMP_BF16");
   if (p->Hkv == 0 || p->Hq % p->Hkv) return fail(LAMP_ERR_UNSUPPORTED, "Hq must be a multiple of Hkv >= 1");
-  if ((p->Hq / p->Hkv) * p->S_q > 32)
-    return fail(LAMP_ERR_UNSUPPORTED, "(Hq/Hkv) * S_q = %lld > 32", (long long)((p->Hq / p->Hkv) * p->S_q));
+  if (product_exceeds({p->Hq / p->Hkv, p->S_q}, 32))
+    return fail(LAMP_ERR_UNSUPPORTED, "(Hq/Hkv) * S_q above 32");
   if (p->tile_m < 1) return fail(LAMP_ERR_SHAPE, "tile_m must be positive");
   if (p->causal && p->S_q > p->S_k) return fail(LAMP_ERR_UNSUPPORTED, "causal needs S_q <= S_k");
   if (p->S_k > kMaxSeq) return fail(LAMP_ERR_UNSUPPORTED, "S_k above %lld", (long long)kMaxSeq);
@@ -436,6 +454,8 @@ static lamp_status decode_prepare(const lamp_decode_params* p, void* workspace, 
     return ok();
   }
   if (p->S_k == 0) return fail(LAMP_ERR_SHAPE, "S_k == 0 with queries");
+  // (before any size is narrowed to 32 bits: B * Hq bounds every one)
+  if (product_exceeds({p->B, p->Hq}, kMaxGrid)) return fail(LAMP_ERR_UNSUPPORTED, "grid too large");
   if (!p->q8 || !p->q_scale || !p->k8 || !p->k_scale || !p->v8 || !p->v_scale || !p->out ||
       (need_ws && !workspace))
     return fail(LAMP_ERR_NULL, "q8, k8, v8, their scales, out and workspace are required");
