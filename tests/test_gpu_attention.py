@@ -237,6 +237,31 @@ def test_exp8_extreme_logit_spread():
         check_head(cfg, P, g, 0, h)
 
 
+def test_max_sequence_length():
+    """The longest supported sequence, 2^20 keys: every in-kernel row index
+    and every K/V byte offset within one head still fits 32 bits (K of one
+    head spans 512 MB at D 256).  A causal chunk of 128 new queries at the
+    end of the context, int8 with a quarter of the groups 16-bit and one
+    group per key tile (16384 groups, 256 mask words per row); codes, scales
+    and mask bit-exact, every output element and LSE against the oracle.
+    Q and K are scaled by 3 (logits of standard deviation 9), so that each
+    row's few largest keys, wherever they lie in the million, dominate its
+    output (|O| near 1): a wrong address at a far key would show."""
+    S_k, S_q = 1 << 20, 128
+    cfg = small_cfg(256, 128, "bf16", "i8", True, 1, 1, 1, S_k, 1, 0.25, input_scale=3.0)
+    q, k, v = make_inputs(cfg, S=S_k)
+    q = q[:, :, S_k - S_q:].contiguous()
+    print("[attn] max sequence length", flush=True)
+    g = gpu_run(cfg, q, k, v)
+    assert g["mask"].shape[-1] == 256
+    P = oracle_problem(cfg, q, k, v)
+    check_codes_and_mask(cfg, P, g)
+    O, _ = A.attn_tilemix(P, 0, 0, np.arange(S_q))
+    assert np.median(np.abs(O).max(axis=1)) > 0.5
+    st = check_head(cfg, P, g, 0, 0)
+    print(f"  max |O - oracle| {st['max_err']:.3e}", flush=True)
+
+
 @pytest.mark.parametrize("case", LAMP, ids=lambda c: "d{}_m{}_{}_{}_x8{}_ad{}_s{}".format(
     c[0], c[1], c[2], c[3], int(c[12]), int(c[13]), c[8]))
 def test_small_lamp(case):

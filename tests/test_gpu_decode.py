@@ -36,15 +36,21 @@ CASES = [
     # the benchmarked step: batch 8, Qwen3-8B heads, one new token over a
     # 32768-token cache (32-tile splits, 16 per (batch, KV head))
     (128, "bf16", 8, 32, 8, 1, 32768, True, 64),
+    # the longest supported cache, 2^20 keys: 16-tile splits, 1024 of them;
+    # Q times 6 (logits of standard deviation 6), so that each query's few
+    # largest keys, wherever they lie, dominate its output
+    (128, "bf16", 1, 8, 1, 1, 1 << 20, True, 64, 6.0),
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "d{}_{}_b{}_h{}x{}_q{}_k{}_{}".format(
     c[0], c[1], c[2], c[3], c[4], c[5], c[6], "causal" if c[7] else "full"))
 def test_decode_parity(case):
-    D, dt, B, Hq, Hkv, S_q, S_k, causal, tm = case
+    D, dt, B, Hq, Hkv, S_q, S_k, causal, tm, *qmul = case
     print(f"[decode] {case}", flush=True)
     q = rand16((B, Hq, S_q, D), 1, DT[dt])
+    if qmul:
+        q = q * qmul[0]
     k = rand16((B, Hkv, S_k, D), 2, DT[dt])
     v = rand16((B, Hkv, S_k, D), 3, DT[dt])
     qd, kd, vd = q.to(dev()), k.to(dev()), v.to(dev())
@@ -63,6 +69,8 @@ def test_decode_parity(case):
     for b in range(B):
         for h in range(Hq):
             O, lse_ref = decode.decode_attention(P, b, h, np.arange(S_q))
+            if qmul:
+                assert np.abs(O).max() > 0.5
             st = compare.check(got[b, h], O, dt)
             assert st["ok"], f"({b},{h}): {st}"
             assert np.abs(glse[b, h] - lse_ref).max() <= 2e-3 + 1e-5 * np.abs(lse_ref).max()
