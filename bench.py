@@ -445,7 +445,7 @@ def other_workloads(torch, L):
         del q, k, v
         sp = Pipeline(L, cfg, qd, kd, vd, torch)
         sp.prep()
-        ts = time_attn(torch, sp, iters=5, warmup=1)
+        ts = time_attn(torch, sp, iters=10, warmup=2, prep_each=True)
         cc = sp.counts()
         tr = roofline_time(cc, cfg.D)
         med = float(np.median(ts))
@@ -650,7 +650,7 @@ def main():
                 sc = get_config("C5", f, code)
                 sp = Pipeline(L, sc, qd, kd, vd, torch)
                 sp.prep()
-                ts = time_attn(torch, sp, iters=5, warmup=1)
+                ts = time_attn(torch, sp, iters=10, warmup=2, prep_each=True)
                 cc = sp.counts()
                 tr = roofline_time(cc, sc.D)
                 sweep[f"{code}_f{int(round(100 * f)):02d}"] = {
@@ -665,7 +665,7 @@ def main():
         sc = get_config("C5", 0.25, "i8")
         sp = Pipeline(L, sc, qd, kd, vd, torch, template=tpl)
         sp.prep()
-        ts = time_attn(torch, sp, iters=5, warmup=1)
+        ts = time_attn(torch, sp, iters=10, warmup=2, prep_each=True)
         cc = sp.counts()
         tr = roofline_time(cc, sc.D)
         sweep["i8_template_sink1_band2_stride5"] = {
@@ -680,7 +680,7 @@ def main():
         lens = (16384, 6000)
         sp = Pipeline(L, sc, qd, kd, vd, torch, seqlens=lens)
         sp.prep()
-        ts = time_attn(torch, sp, iters=5, warmup=1)
+        ts = time_attn(torch, sp, iters=10, warmup=2, prep_each=True)
         cc = sp.counts()
         tr = roofline_time(cc, sc.D)
         sweep["i8_f25_varlen_16384_6000"] = {
@@ -695,7 +695,7 @@ def main():
             sc = get_config("C5", f, "e4m3")
             sp = Pipeline(L, sc, qd, kd, vd, torch, pv8=True)
             sp.prep()
-            ts = time_attn(torch, sp, iters=5, warmup=1)
+            ts = time_attn(torch, sp, iters=10, warmup=2, prep_each=True)
             cc = sp.counts()
             tr = roofline_time_pv8(cc, sc.D)
             sweep[f"e4m3_f{int(round(100 * f)):02d}_pv8"] = {
