@@ -32,6 +32,17 @@ Logits (fp64):
             product is a multiple of 2**-18 below 2**18 and at most 256 terms
             are summed)
 
+Tolerances (for the comparison with an fp32 evaluation): every logit carries
+a rigorous bound on its evaluation error (fp32 sums of the exact products in
+any order, the gfx950 matrix cores' cut of e4m3 products, the fp32 scale
+roundings).  ``attn_lamp`` takes every flag decision whose margin lies within
+its bound both ways (one branch per outcome), and widens each output element
+by the exact effect of moving every weight as far as its logit's bound
+allows: the e4m3 rounding flips one by one, the relative weight errors through
+Cauchy-Schwarz on running moments of V, all in the frame of the final running
+maximum.  The LSE bound adds the maximum's, the exponents' and the flips'
+shares to the rounding of the sum and the logarithm.
+
 Readings where the pages are silent (listed in the design notes): causal
 aligns the queries with the end of the keys, as for a chunk of S_q new
 queries after S_k - S_q earlier tokens: query i sits at key position
