@@ -310,12 +310,18 @@ def _err_logits_tilemix(P, b, h, rows, cols, s, r8, m_row):
 
 
 def tilemix_bounds(P, b, h, rows, dtype="bf16"):
-    """``attn_tilemix`` with a bound on the LSE error of an fp32 evaluation
-    whose exponents carry errors within ``_err_logits_tilemix``: at most
+    """``attn_tilemix`` with bounds for an fp32 evaluation whose exponents
+    carry errors within ``_err_logits_tilemix`` (E).
+
+    The evaluation's weights share one reference (a common factor O does not
+    see), so weight k is p_k exp(d_k) with |d_k| <= E_k, and O moves by
+    sum_k p_k (exp(d_k) - 1) (v_k - O) / sum_k p_k exp(d_k): at most
+    sqrt(sum p eps^2) sqrt(sum p (v - O)^2) / (l - sum p eps) per element
+    (eps = expm1(E), Cauchy-Schwarz), the widening.  The LSE moves by at most
     max_j E_j, plus half an ulp of the 16-bit weights that the normaliser
     sums, fp16 subnormal weights (2^-25 each against l >= 1) and fp32
     rounding of the sum and the logarithm.  Returns (O [R, D], LSE [R],
-    lse_tol [R])."""
+    lse_tol [R], widening [R, D])."""
     rows = np.asarray(rows)
     s, r8, ok = routed_logits(P, b, h, rows)
     none = ~ok.any(axis=1)
@@ -326,7 +332,16 @@ def tilemix_bounds(P, b, h, rows, dtype="bf16"):
     sub16 = 0.0 if dtype == "bf16" else ok.sum(axis=1) * 2.0 ** -25
     lse_tol = (E.max(axis=1, initial=0.0) + np.log1p(_sum16_rel(dtype)) + sub16
                + (P.n_kt + 64) * U32 + 4 * U32 * np.abs(np.where(none, 0.0, lse)))
-    return O, lse, lse_tol
+    p = np.where(ok, np.exp(sf - m[:, None]), 0.0)
+    eps = np.expm1(E)
+    pe = p * eps
+    vh = P.v[b, P.kvh(h)]
+    l = p.sum(axis=1)
+    dev2 = p @ (vh * vh) - 2.0 * O * (p @ vh) + O * O * l[:, None]
+    num = np.sqrt((pe * eps).sum(axis=1))[:, None] * np.sqrt(np.maximum(dev2, 0.0))
+    denom = np.maximum(l - pe.sum(axis=1), 1e-300)
+    extra = np.where(none[:, None], 0.0, num / denom[:, None])
+    return O, lse, lse_tol, extra
 
 
 # ---------------------------------------------------------------------------

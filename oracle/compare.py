@@ -2,10 +2,10 @@
 
 |O_gpu - O_ref| <= max(atol, ulp_dtype(O_ref)) + extra, element by element,
 where atol is 2e-3 for fp16 outputs and 1e-2 for bf16 outputs, and extra is
-the widening on the LampAttention paths for what the weights may move by
-within the logit error bounds (e4m3 rounding flips, e4m3 weights at a
-running maximum that may be off, fp32 weights' exponent errors; zero on the
-TileMix path).  One unit in the last place of the output dtype
+the widening for what the weights may move by within the logit error bounds
+(on the LampAttention paths: e4m3 rounding flips, e4m3 weights at a running
+maximum that may be off, fp32 weights' exponent errors; on the TileMix path:
+the exponents' errors, ``attention.tilemix_bounds``).  One unit in the last place of the output dtype
 covers the final rounding of O itself when |O| is large enough that half an
 ulp exceeds atol (bf16: |O| >= 2).
 
@@ -26,20 +26,22 @@ def ulp(x, dtype):
     return 2.0 ** (e - MANT[dtype])
 
 
-def tolerance(O_ref, dtype, extra_row=None):
+def tolerance(O_ref, dtype, extra=None):
+    """max(atol, ulp(O_ref)) plus the widening extra (per element, or per
+    row)."""
     tol = np.maximum(ATOL[dtype], ulp(O_ref, dtype))
-    if extra_row is not None:
-        e = np.asarray(extra_row)
+    if extra is not None:
+        e = np.asarray(extra)
         tol = tol + (e if e.ndim == np.ndim(O_ref) else e[..., None])
     return tol
 
 
-def check(O_gpu, O_ref, dtype, extra_row=None, exclude_rows=None):
+def check(O_gpu, O_ref, dtype, extra=None, exclude_rows=None):
     """Returns a stats dict; stats['ok'] is the pass/fail decision."""
     O_gpu = np.asarray(O_gpu, dtype=np.float64)
     O_ref = np.asarray(O_ref, dtype=np.float64)
     err = np.abs(O_gpu - O_ref)
-    tol = tolerance(O_ref, dtype, extra_row)
+    tol = tolerance(O_ref, dtype, extra)
     bad = err > tol
     if exclude_rows is not None:
         bad = bad & ~np.asarray(exclude_rows)[..., None]
@@ -77,7 +79,7 @@ def check_lamp(res, O_gpu, dtype, flags_gpu=None, lse_gpu=None, keep=None):
               n_branches=sum(len(b) for b in res.branches), n_nonprimary=0,
               unresolved=int(res.unresolved.sum()), excluded_rows=0,
               max_extra=float(res.extra_tol.max()) if res.extra_tol.size else 0.0,
-              finite=bool(np.isfinite(O_gpu).all()))
+              n_elems=0, n_wide=0, finite=bool(np.isfinite(O_gpu).all()))
     if not st["finite"]:
         st["ok"] = False
     for i, (brs, idx) in enumerate(zip(res.branches, res.row_branch)):
@@ -110,6 +112,9 @@ def check_lamp(res, O_gpu, dtype, flags_gpu=None, lse_gpu=None, keep=None):
         j, err, good, lse_ok = best
         if j != 0:
             st["n_nonprimary"] += 1
+        # elements whose tolerance the widening takes beyond atol
+        st["n_elems"] += int(kp.sum()) * err.shape[1]
+        st["n_wide"] += int(((brs[j].extra_tol > ATOL[dtype]) & kp[:, None]).sum())
         st["max_err"] = max(st["max_err"], float(err.max()) if err.size else 0.0)
         st["n_bad"] += int((~good).sum())
         st["n_ulp_branch"] += int(((err > ATOL[dtype]) & good).sum())

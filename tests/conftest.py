@@ -30,7 +30,8 @@ def pytest_collection_modifyitems(config, items):
 def pytest_terminal_summary(terminalreporter, exitstatus, config):
     """One line with the LampAttention acceptance counts of the GPU parity
     tests (flag decisions within the error bound evaluated both ways, flag
-    mismatches, rows excluded, widening for e4m3 rounding flips)."""
+    mismatches, rows excluded, the widening for what the weights may move by
+    within the logit bounds, and how many elements it takes beyond atol)."""
     try:
         from gpu_util import LAMP_REPORT
     except Exception:  # pragma: no cover
@@ -40,7 +41,9 @@ def pytest_terminal_summary(terminalreporter, exitstatus, config):
         terminalreporter.write_line(
             "lamp acceptance: sub-blocks {} | decisions within the error bound (both ways) {} | "
             "non-primary branches picked {} | flag mismatches {} | branch-cap overflows {} | "
-            "rows excluded {} | max widening {:.2e} | max |O - oracle| {:.2e}".format(
+            "rows excluded {} | max widening {:.2e} | elements widened beyond atol {} of {} | "
+            "max |O - oracle| {:.2e}".format(
                 r.get("n_subblocks", 0), r.get("n_split", 0), r.get("n_nonprimary", 0),
                 r.get("flag_mismatch", 0), r.get("unresolved", 0), r.get("excluded_rows", 0),
-                r.get("max_extra", 0.0), r.get("max_err", 0.0)))
+                r.get("max_extra", 0.0), r.get("n_wide", 0), r.get("n_elems", 0),
+                r.get("max_err", 0.0)))

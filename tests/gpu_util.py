@@ -21,7 +21,7 @@ def record_lamp(st):
             f.write(json.dumps({"test": os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0],
                                 **{k: v for k, v in st.items()}}) + "\n")
     for k in ("n_subblocks", "n_split", "n_branches", "n_nonprimary", "flag_mismatch",
-              "unresolved", "excluded_rows", "lse_bad", "n_bad"):
+              "unresolved", "excluded_rows", "lse_bad", "n_bad", "n_elems", "n_wide"):
         LAMP_REPORT[k] = LAMP_REPORT.get(k, 0) + int(st.get(k, 0))
     LAMP_REPORT["max_extra"] = max(LAMP_REPORT.get("max_extra", 0.0), float(st.get("max_extra", 0.0)))
     LAMP_REPORT["max_err"] = max(LAMP_REPORT.get("max_err", 0.0), float(st.get("max_err", 0.0)))

@@ -79,8 +79,8 @@ def check_head(cfg, P, g, b, h, rows=None, sub_blocks=None, report=None):
         assert st["ok"], f"head ({b},{h}): {st}"
     else:
         rr = np.arange(P.S_q) if rows is None else np.asarray(rows)
-        O, lse_ref, lse_tol = A.tilemix_bounds(P, pb, ph, rr, cfg.dtype)
-        st = compare.check(got[rr], O, cfg.dtype)
+        O, lse_ref, lse_tol, extra = A.tilemix_bounds(P, pb, ph, rr, cfg.dtype)
+        st = compare.check(got[rr], O, cfg.dtype, extra)
         assert st["ok"], f"head ({b},{h}): {st}"
         if g["lse"] is not None:
             check_lse(g["lse"][b, h][rr], lse_ref, lse_tol)
@@ -318,6 +318,62 @@ def test_small_pv8(case):
 
 
 # ---------------------------------------------------------------------------
+# seeded random configurations across the supported space, every element
+# ---------------------------------------------------------------------------
+
+MODES = ("tilemix", "exp8", "adaptive", "adaptive_exp8", "pv8")
+
+
+def random_case(i):
+    """Configuration i of the sweep, drawn from a generator seeded with i:
+    head dim, tile height, 16-bit type, 8-bit code, mode, causal or not,
+    batch and GQA shape, ragged lengths (S_q <= S_k when causal), group size,
+    16-bit fraction, and the outlier/sink recipe or plain N(0, 1) inputs."""
+    rng = np.random.default_rng(zlib.crc32(b"random-config") + i)
+    D = int(rng.choice([64, 128, 256]))
+    tm = int(rng.choice([64, 128]))
+    dt = str(rng.choice(["bf16", "f16"]))
+    code = str(rng.choice(["i8", "e4m3"]))
+    mode = MODES[i % len(MODES)]
+    causal = bool(rng.integers(2))
+    B = int(rng.integers(1, 3))
+    Hkv = int(rng.integers(1, 3))
+    Hq = Hkv * int(rng.choice([1, 2, 4]))
+    S_k = int(rng.integers(1, 700))
+    S_q = int(rng.integers(1, S_k + 1)) if causal else int(rng.integers(1, 700))
+    G = int(rng.choice([1, 2, 4]))
+    f16 = float(rng.choice([0.0, 0.3, 1.0]))
+    outl = bool(rng.integers(2))
+    return D, tm, dt, code, mode, causal, B, Hq, Hkv, S_q, S_k, G, f16, outl
+
+
+@pytest.mark.parametrize("i", range(100), ids=lambda i: "cfg{:02d}".format(i))
+def test_random_config(i):
+    D, tm, dt, code, mode, causal, B, Hq, Hkv, S_q, S_k, G, f16, outl = random_case(i)
+    exp8 = mode in ("exp8", "adaptive_exp8", "pv8")
+    ad = mode.startswith("adaptive")
+    pv8 = mode == "pv8"
+    cfg = small_cfg(D, tm, dt, code, causal, B, Hq, Hkv, max(S_q, S_k), G, f16, exp8=exp8,
+                    adaptive=ad, outliers=outl, seed=100 + i)
+    if f16 == 0.0:
+        cfg = cfg.with_(mask_all_ones=True)
+    q, k, v = inputs_qk(cfg, S_q, S_k)
+    print(f"[attn] random {i}: {random_case(i)}", flush=True)
+    g = gpu_run(cfg, q, k, v, pv8=pv8)
+    P = oracle_problem(cfg, q, k, v, pv8=pv8)
+    check_codes_and_mask(cfg, P, g)
+    if pv8:
+        from oracle import quant as oq
+        assert (g["v8"] == oq.pack_v_tiles(P.v_codes)).all() and (g["vs"] == P.v_scales).all()
+    rep = {}
+    for b in range(B):
+        for h in range(Hq):
+            check_head(cfg, P, g, b, h, report=rep)
+    if rep:
+        print(f"  lamp report {rep}", flush=True)
+
+
+# ---------------------------------------------------------------------------
 # full-size configurations, sampled query tiles
 # ---------------------------------------------------------------------------
 
@@ -546,8 +602,8 @@ def test_varlen(case):
                 rows, lse_ref = rr[keep], res.lse[keep]
             else:
                 rows = np.arange(Lq[b])
-                O_ref, lse_ref, lse_tol = A.tilemix_bounds(P, b, h, rows, dt)
-                st = compare.check(got[b, h][rows], O_ref, dt)
+                O_ref, lse_ref, lse_tol, extra = A.tilemix_bounds(P, b, h, rows, dt)
+                st = compare.check(got[b, h][rows], O_ref, dt, extra)
                 check_lse(glse[b, h][rows], lse_ref, lse_tol)
             assert st["ok"], f"varlen ({b},{h}): {st}"
             none = np.isneginf(lse_ref)

@@ -255,8 +255,11 @@ def test_bounds_not_vacuous_on_adaptive_workload():
 
 def test_tilemix_lse_bound_small_on_normal_inputs():
     P = problem(D=128, S=1024, code="i8", outliers=False, adaptive=False, exp8=False, f16=0.25)
-    _, _, lse_tol = A.tilemix_bounds(P, 0, 1, np.arange(1024))
+    _, _, lse_tol, extra = A.tilemix_bounds(P, 0, 1, np.arange(1024))
     assert lse_tol.max() < 5e-3
+    # int8 products are exact; the 16-bit tiles' fp32 sums and the scale
+    # roundings leave a widening far below atol
+    assert extra.max() < 1e-3
 
 
 # ---------------------------------------------------------------------------
@@ -327,20 +330,50 @@ def test_perturbed_within_bound_is_accepted_adaptive_workload_shape(edge):
         assert st["ok"], st
 
 
-def test_perturbed_tilemix_lse_within_bound():
+@pytest.mark.parametrize("code,D,f16,scale,dtype", [("i8", 128, 0.3, 3.0, "bf16"),
+                                                   ("e4m3", 256, 0.0, 1.0, "f16"),
+                                                   ("e4m3", 128, 0.3, 1.0, "bf16")])
+def test_perturbed_tilemix_within_bound(code, D, f16, scale, dtype):
+    # every logit moved by up to 99.9% of its bound (uniform, then at the
+    # edges): the LSE stays within lse_tol and O within atol + the widening
     rng = np.random.default_rng(7)
-    P = problem(D=128, S=768, code="i8", outliers=True, adaptive=False, exp8=False, f16=0.3,
-                scale=3.0)
+    P = problem(D=D, S=768 if D == 128 else 512, code=code, outliers=True, adaptive=False,
+                exp8=False, f16=f16, scale=scale, dtype=dtype)
     rows = np.arange(P.S_q)
-    O, lse, lse_tol = A.tilemix_bounds(P, 0, 0, rows)
+    O, lse, lse_tol, extra = A.tilemix_bounds(P, 0, 0, rows, dtype)
     s, r8, ok = A.routed_logits(P, 0, 0, rows)
     m = np.where(ok, s, -np.inf).max(axis=1)
     E = A._err_logits_tilemix(P, 0, 0, rows, np.arange(P.S_k), np.where(ok, s, 0), r8, m)
-    for _ in range(4):
-        sp = np.where(ok, s + rng.uniform(-0.999, 0.999, s.shape) * E, -np.inf)
+    vh = P.v[0, 0]
+    for edge in (False, True, False, True):
+        u = np.where(rng.random(s.shape) < 0.5, -0.999, 0.999) if edge else \
+            rng.uniform(-0.999, 0.999, s.shape)
+        sp = np.where(ok, s + u * E, -np.inf)
         mp = sp.max(axis=1)
-        lsep = mp + np.log(np.exp(sp - mp[:, None]).sum(axis=1))
+        pp = np.exp(sp - mp[:, None])
+        lsep = mp + np.log(pp.sum(axis=1))
         assert (np.abs(lsep - lse) <= lse_tol).all()
+        Op = (pp @ vh) / pp.sum(axis=1)[:, None]
+        assert compare.check(Op, O, dtype, extra)["ok"]
+
+
+def test_tilemix_widening_covers_the_matrix_core_cut():
+    # e4m3 at head dim 256 on the outlier recipe, every tile 8-bit: logits
+    # summed as the matrix cores were measured to sum them (the cut) move O
+    # by more than atol, and stay within atol + the widening
+    P = problem(D=256, S=512, code="e4m3", outliers=True, adaptive=False, exp8=False, f16=0.0,
+                dtype="f16", seed=145)
+    rows, cols = np.arange(P.S_q), np.arange(P.S_k)
+    O, _, _, extra = A.tilemix_bounds(P, 0, 0, rows, "f16")
+    acc = f8_matrix_core_dot(P.qv[0, 0], P.kv[0, 0]).astype(np.float64)
+    sq = P.q_scales[0, 0].astype(np.float64)[rows // P.tile_m]
+    sk = P.k_scales[0, 0].astype(np.float64)[cols // P.tile_n]
+    s = np.where(P.valid(rows, cols, 0), acc * sq[:, None] * sk[None, :] * P.sm_scale, -np.inf)
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    Oc = (p @ P.v[0, 0]) / p.sum(axis=1)[:, None]
+    assert not compare.check(Oc, O, "f16")["ok"]
+    assert compare.check(Oc, O, "f16", extra)["ok"]
+    assert extra.max() < 0.25
 
 
 # ---------------------------------------------------------------------------
