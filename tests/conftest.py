@@ -33,9 +33,17 @@ def pytest_terminal_summary(terminalreporter, exitstatus, config):
     mismatches, rows excluded, the widening for what the weights may move by
     within the logit bounds, and how many elements it takes beyond atol)."""
     try:
-        from gpu_util import LAMP_REPORT
+        from gpu_util import LAMP_REPORT, PATH_REPORT
     except Exception:  # pragma: no cover
         return
+    for path, r in sorted(PATH_REPORT.items()):
+        terminalreporter.write_line(
+            "{} acceptance: elements {} | max |O - oracle| {:.2e} ({}) | elements beyond atol {} | "
+            "elements widened beyond atol {} | max widening {:.2e} ({}) | max LSE deviation {:.2e} "
+            "({:.2f} of its bound)".format(
+                path, r.get("n_elems", 0), r.get("max_err", 0.0), r.get("max_err_test", "-"),
+                r.get("n_over_atol", 0), r.get("n_wide", 0), r.get("max_extra", 0.0),
+                r.get("max_extra_test", "-"), r.get("max_lse_dev", 0.0), r.get("max_lse_ratio", 0.0)))
     if LAMP_REPORT:
         r = LAMP_REPORT
         terminalreporter.write_line(
@@ -47,3 +55,6 @@ def pytest_terminal_summary(terminalreporter, exitstatus, config):
                 r.get("flag_mismatch", 0), r.get("unresolved", 0), r.get("excluded_rows", 0),
                 r.get("max_extra", 0.0), r.get("n_wide", 0), r.get("n_elems", 0),
                 r.get("max_err", 0.0)))
+        terminalreporter.write_line(
+            "lamp largest widening in {}; largest |O - oracle| in {}".format(
+                r.get("max_extra_test", "-"), r.get("max_err_test", "-")))

@@ -23,8 +23,45 @@ def record_lamp(st):
     for k in ("n_subblocks", "n_split", "n_branches", "n_nonprimary", "flag_mismatch",
               "unresolved", "excluded_rows", "lse_bad", "n_bad", "n_elems", "n_wide"):
         LAMP_REPORT[k] = LAMP_REPORT.get(k, 0) + int(st.get(k, 0))
-    LAMP_REPORT["max_extra"] = max(LAMP_REPORT.get("max_extra", 0.0), float(st.get("max_extra", 0.0)))
-    LAMP_REPORT["max_err"] = max(LAMP_REPORT.get("max_err", 0.0), float(st.get("max_err", 0.0)))
+    test = _current_test()
+    for k in ("max_extra", "max_err"):
+        v = float(st.get(k, 0.0))
+        if v >= LAMP_REPORT.get(k, 0.0):
+            LAMP_REPORT[k] = v
+            LAMP_REPORT[k + "_test"] = test
+
+
+def _current_test():
+    return os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0].split("::")[-1]
+
+
+# Acceptance of the paths checked element by element against one oracle
+# output (TileMix: the mask paths with fp32 exponentials; decode): elements
+# compared, the largest error, how many exceed atol (accepted through one
+# ulp of the output dtype or the widening for the exponents' error bounds),
+# the largest widening, and the largest LSE deviation relative to its bound.
+PATH_REPORT = {}
+
+
+def record_path(path, st, O_gpu, O_ref, dtype, extra=None, lse_dev=None, lse_tol=None):
+    from oracle import compare
+    r = PATH_REPORT.setdefault(path, {})
+    err = np.abs(np.asarray(O_gpu, dtype=np.float64) - np.asarray(O_ref, dtype=np.float64))
+    r["n_elems"] = r.get("n_elems", 0) + int(err.size)
+    r["n_over_atol"] = r.get("n_over_atol", 0) + int((err > compare.ATOL[dtype]).sum())
+    test = _current_test()
+    if err.size and float(err.max()) >= r.get("max_err", 0.0):
+        r["max_err"], r["max_err_test"] = float(err.max()), test
+    if extra is not None:
+        e = np.broadcast_to(np.asarray(extra, dtype=np.float64), err.shape) if np.ndim(extra) == err.ndim \
+            else np.broadcast_to(np.asarray(extra, dtype=np.float64)[..., None], err.shape)
+        r["n_wide"] = r.get("n_wide", 0) + int((e > compare.ATOL[dtype]).sum())
+        if e.size and float(e.max()) >= r.get("max_extra", 0.0):
+            r["max_extra"], r["max_extra_test"] = float(e.max()), test
+    if lse_dev is not None and np.size(lse_dev):
+        ratio = float(np.max(np.asarray(lse_dev) / np.maximum(np.asarray(lse_tol), 1e-300)))
+        r["max_lse_dev"] = max(r.get("max_lse_dev", 0.0), float(np.max(lse_dev)))
+        r["max_lse_ratio"] = max(r.get("max_lse_ratio", 0.0), ratio)
 
 from oracle import attention as A
 from oracle import mask as omask

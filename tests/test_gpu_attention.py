@@ -20,7 +20,7 @@ import torch
 
 import zlib
 
-from gpu_util import device, gpu_run, oracle_mask, oracle_problem, record_lamp, u64
+from gpu_util import device, gpu_run, oracle_mask, oracle_problem, record_lamp, record_path, u64
 from oracle import attention as A
 from oracle import compare
 from oracle import mask as omask
@@ -82,8 +82,13 @@ def check_head(cfg, P, g, b, h, rows=None, sub_blocks=None, report=None):
         O, lse_ref, lse_tol, extra = A.tilemix_bounds(P, pb, ph, rr, cfg.dtype)
         st = compare.check(got[rr], O, cfg.dtype, extra)
         assert st["ok"], f"head ({b},{h}): {st}"
+        lse_dev = None
         if g["lse"] is not None:
             check_lse(g["lse"][b, h][rr], lse_ref, lse_tol)
+            fin = np.isfinite(lse_ref)
+            lse_dev = np.abs(g["lse"][b, h][rr][fin] - lse_ref[fin])
+            lse_tol = lse_tol[fin]
+        record_path("tilemix", st, got[rr], O, cfg.dtype, extra, lse_dev, lse_tol)
     return st
 
 
@@ -605,6 +610,9 @@ def test_varlen(case):
                 O_ref, lse_ref, lse_tol, extra = A.tilemix_bounds(P, b, h, rows, dt)
                 st = compare.check(got[b, h][rows], O_ref, dt, extra)
                 check_lse(glse[b, h][rows], lse_ref, lse_tol)
+                fin = np.isfinite(lse_ref)
+                record_path("tilemix", st, got[b, h][rows], O_ref, dt, extra,
+                            np.abs(glse[b, h][rows][fin] - lse_ref[fin]), lse_tol[fin])
             assert st["ok"], f"varlen ({b},{h}): {st}"
             none = np.isneginf(lse_ref)
             assert (got[b, h][rows][none] == 0).all()

@@ -5,6 +5,7 @@ import pytest
 import torch
 
 from oracle import compare, decode
+from gpu_util import record_path
 
 pytestmark = pytest.mark.gpu
 
@@ -73,7 +74,10 @@ def test_decode_parity(case):
                 assert np.abs(O).max() > 0.5
             st = compare.check(got[b, h], O, dt)
             assert st["ok"], f"({b},{h}): {st}"
-            assert np.abs(glse[b, h] - lse_ref).max() <= 2e-3 + 1e-5 * np.abs(lse_ref).max()
+            lse_tol = 2e-3 + 1e-5 * np.abs(lse_ref).max()
+            lse_dev = np.abs(glse[b, h] - lse_ref)
+            assert lse_dev.max() <= lse_tol
+            record_path("decode", st, got[b, h], O, dt, None, lse_dev, np.full(lse_dev.shape, lse_tol))
 
 
 def test_decode_graph_replay_matches_eager():
